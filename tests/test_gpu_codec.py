@@ -1,0 +1,148 @@
+"""GPU parity of the codec entry points against the oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _parity import code_steps, log, rel_err
+
+pytestmark = pytest.mark.gpu
+E4, E5, NOEXP = 0, 1, 0x100
+FMTS = [E4, E5]
+FPMAX = {E4: 448.0, E5: 57344.0}
+
+
+@pytest.fixture(scope="module")
+def coat():
+    import fp8_optimizer_state_amd as c
+    assert torch.cuda.is_available()
+    c.lib()
+    return c
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_decode_all_codes(coat, fmt):
+    log(f"test_decode_all_codes fmt={fmt}")
+    q = torch.arange(256, dtype=torch.uint8, device="cuda")
+    y = torch.empty(256, dtype=torch.float32, device="cuda")
+    coat.decode(q, y, fmt=fmt)
+    got = y.cpu().numpy().astype(np.float64)
+    want = oracle.fp8_decode(np.arange(256, dtype=np.uint8), fmt)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    fin = ~np.isnan(want)
+    assert np.array_equal(got[fin], want[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(want[fin]))
+
+
+def encode_cases(fmt, seed=0):
+    """Every finite code value and the midpoints between neighbours with their
+    fp32 neighbours, strided sweeps over the fp32 range, and specials."""
+    vals = oracle.fp8_decode(np.arange(128, dtype=np.uint8), fmt)
+    top = 0x7E if fmt == E4 else 0x7B
+    grid = vals[:top + 1].astype(np.float32)
+    mids = (0.5 * (vals[:top] + vals[1:top + 1])).astype(np.float32)  # exact in fp32
+    near = []
+    for base in (grid, mids):
+        b = base.astype(np.float32)
+        for k in range(1, 4):
+            up, dn = b.copy(), b.copy()
+            for _ in range(k):
+                up = np.nextafter(up, np.float32(np.inf))
+                dn = np.nextafter(dn, np.float32(-np.inf))
+            near += [up, dn]
+    rng = np.random.default_rng(seed)
+    sweep = np.arange(0x30000000, 0x48000000, 997, dtype=np.uint32).view(np.float32)  # ~2^-31 .. 2^17
+    rnd = (10.0 ** rng.uniform(-12, 6, 200000)).astype(np.float32)
+    spec = np.array([0.0, np.inf, FPMAX[fmt] * 2, FPMAX[fmt] * 1.04, 1e-45, 1e-40, 3e38],
+                    np.float32)
+    y = np.concatenate([grid, mids, *near, sweep, rnd, spec])
+    y = np.concatenate([y, -y, np.array([np.nan], np.float32)])
+    return y
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_encode_is_exact_rne_saturating(coat, fmt):
+    y = encode_cases(fmt)
+    log(f"test_encode fmt={fmt} n={y.size}")
+    Y = torch.from_numpy(y).cuda()
+    Q = torch.empty(y.size, dtype=torch.uint8, device="cuda")
+    coat.encode(Y, Q, fmt=fmt)
+    got = Q.cpu().numpy()
+    want = oracle.fp8_encode(y.astype(np.float64), fmt)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(float(y[i]), hex(got[i]), hex(want[i])) for i in bad[:10]]
+
+
+def page_like(n, G, kind, seed):
+    rng = np.random.default_rng(seed)
+    ng = (n + G - 1) // G
+    scale = np.repeat(10.0 ** rng.uniform(-5, -2, ng), G)[:n]
+    if kind == "m":
+        x = np.where(rng.random(n) < 0.5, -1.0, 1.0) * scale * 10.0 ** rng.uniform(-3, 0, n)
+    else:
+        x = scale * scale * 10.0 ** rng.uniform(-1, 0, n)
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", [E4, E5, E4 | NOEXP, E5 | NOEXP])
+@pytest.mark.parametrize("G", [16, 32, 64, 128, 256, 1024])
+@pytest.mark.parametrize("n", [1, 1000, 1024 * 37 + 333])
+def test_quantize_parity(coat, fmt, G, n):
+    for kind in ("m", "v"):
+        x = page_like(n, G, kind, seed=G + n + fmt)
+        log(f"test_quantize_parity fmt={fmt:#x} G={G} n={n} kind={kind}")
+        X = torch.from_numpy(x).cuda()
+        ng = (n + G - 1) // G
+        Q = torch.empty(n, dtype=torch.uint8, device="cuda")
+        S = torch.empty(ng, dtype=torch.float64, device="cuda")
+        K = torch.empty(ng, dtype=torch.float32, device="cuda")
+        coat.quantize(X, Q, S, K, group=G, fmt=fmt)
+        q, s, k = oracle.quantize(x.astype(np.float64), G, fmt)
+        assert rel_err(K.cpu().numpy(), k).max() <= 1e-5
+        assert rel_err(S.cpu().numpy(), s).max() <= 1e-5
+        d = code_steps(Q.cpu().numpy(), q)
+        assert d.max() <= 1 and (d != 0).mean() <= 1e-4
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+@pytest.mark.parametrize("G", [32, 128])
+def test_dequantize_parity(coat, fmt, G):
+    n = 1024 * 50 + 77
+    x = page_like(n, G, "m", seed=5)
+    q, s, k = oracle.quantize(x.astype(np.float64), G, fmt)
+    log(f"test_dequantize_parity fmt={fmt} G={G}")
+    X = torch.empty(n, dtype=torch.float32, device="cuda")
+    coat.dequantize(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda(), torch.from_numpy(k).cuda(),
+                    X, group=G, fmt=fmt)
+    got = X.cpu().numpy().astype(np.float64)
+    want = oracle.dequantize(q, s, k, G, fmt)
+    # fp32 output of an fp64 value: one rounding, so within one fp32 ulp of the oracle
+    assert np.all(np.abs(got - want) <= np.spacing(np.abs(want).astype(np.float32)).astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_quantize_degenerate_groups(coat, fmt):
+    G = 32
+    groups = [
+        np.zeros(G),                                      # all zero
+        np.r_[np.zeros(G - 1), -3e-4],                    # one nonzero
+        1e-3 * (1 + np.linspace(0, 0.9e-6, G)),           # near-constant
+        np.r_[1.0, 1e-30, np.full(G - 2, 1e-3)],          # wider than the FP8 range: k < 1
+        1e-35 * (1 + np.linspace(0, 1, G)),               # tiny narrow group: range guard
+        np.r_[np.full(G - 1, 1e-3), np.nan],              # poisoned
+        np.r_[np.full(G - 1, 1e-3), np.inf],
+        np.r_[np.full(G // 2, 0.0), 10.0 ** -np.arange(G // 2)],
+    ]
+    x = np.concatenate(groups).astype(np.float32)
+    x[3] = -0.0
+    n = x.size
+    log(f"test_quantize_degenerate_groups fmt={fmt}")
+    X = torch.from_numpy(x).cuda()
+    Q = torch.empty(n, dtype=torch.uint8, device="cuda")
+    S = torch.empty(n // G, dtype=torch.float64, device="cuda")
+    K = torch.empty(n // G, dtype=torch.float32, device="cuda")
+    coat.quantize(X, Q, S, K, group=G, fmt=fmt)
+    q, s, k = oracle.quantize(x.astype(np.float64), G, fmt)
+    assert rel_err(K.cpu().numpy(), k).max() <= 1e-5, (K.cpu().numpy(), k)
+    assert rel_err(S.cpu().numpy(), s).max() <= 1e-5, (S.cpu().numpy(), s)
+    assert np.array_equal(Q.cpu().numpy(), q)
