@@ -1,0 +1,226 @@
+"""Benchmark of the fused FP8-state AdamW step on one MI355X.
+
+Workload (default): the Llama-2-13B parameter list (13,015,864,320 params in
+363 tensors), group 128, first moment E4M3 and second moment E5M2, fp32
+master weights, bf16 grads in, bf16 weight copy out; synthetic seeded inputs
+resident in HBM (about 133 GB). One step = one multi-tensor launch over the
+whole list. Prints one JSON line on stdout; progress goes to stderr.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama13b]
+                  [--no-cpu-baseline] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "coat_step_multi_llama13b_pmc.json")
+KERNEL_SRC = os.path.join(ROOT, "fp8_optimizer_state_amd", "csrc", "coat_fp8.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(workload: str, n_launch_bytes: float):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(PMC_FILE) as f:
+            pmc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if pmc.get("source_sha256") != kernel_source_hash() or pmc.get("workload") != workload:
+        return None
+    return pmc.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, per_tensor: int = 229376) -> dict:
+    """The oracle, single-threaded, on a bounded sample of the workload: the
+    first `per_tensor` elements of every tensor (about 65M params for the
+    13B list, 10-20 s of CPU work), prior state quantized by the oracle beforehand (untimed)."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    F32 = lambda x: float(np.float32(x))
+    h = synth.HYPER
+    G = wl.group
+    chunks = []
+    for i, n in enumerate(wl.sizes):
+        c = min(n, per_tensor)
+        p = synth.params(c, wl.seed, i).numpy()
+        g = synth.grads(c, wl.seed, i).view(__import__("torch").int16).numpy().view(np.uint16)
+        m, v = synth.prior_moments(c, G, wl.seed, i)
+        chunks.append((p, g, m.numpy(), v.numpy()))
+    p = np.concatenate([c[0] for c in chunks])
+    g = np.concatenate([c[1] for c in chunks])
+    # every chunk is a whole number of groups, so concatenation keeps group boundaries
+    mq, ms, mk = oracle.quantize_threaded(np.concatenate([c[2] for c in chunks]), G, wl.fmt_m, 8)
+    vq, vs, vk = oracle.quantize_threaded(np.concatenate([c[3] for c in chunks]), G, wl.fmt_v, 8)
+    n = p.size
+    log(f"cpu baseline: oracle on {n} params, 1 thread")
+    t0 = time.perf_counter()
+    oracle.adamw_step(p, g, mq, ms, mk, vq, vs, vk, G, wl.fmt_m, wl.fmt_v, F32(h["lr"]), F32(h["b1"]),
+                      F32(h["b2"]), F32(h["eps"]), F32(h["wd"]), h["step"], threads=1)
+    dt = time.perf_counter() - t0
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": n / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {per_tensor} elements of each of the {len(wl.sizes)} tensors "
+                      f"({n} params), one step, single-threaded fp64 C oracle; {dt:.1f} s on {cpu}",
+            "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama13b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the step shards by whole groups with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import fp8_optimizer_state_amd as coat
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    coat.lib()
+    G = wl.group
+    log(f"workload {wl.name}: {wl.n_params} params, {len(wl.sizes)} tensors")
+
+    # ---- resident state and inputs, generated on the device
+    t0 = time.perf_counter()
+    st = coat.ParamListState(wl.sizes, G, device=dev)
+    for i, n in enumerate(wl.sizes):
+        t = st.tensor(i)
+        synth.params(n, wl.seed, i, device=dev, out=t.params)
+        synth.grads(n, wl.seed, i, device=dev, out=t.grads)
+        m, v = synth.prior_moments(n, G, wl.seed, i, device=dev)
+        coat.quantize(m, t.m_q, t.m_s, t.m_k, group=G, fmt=wl.fmt_m)
+        coat.quantize(v, t.v_q, t.v_s, t.v_k, group=G, fmt=wl.fmt_v)
+        del m, v
+        if i % 60 == 0:
+            log(f"  generated tensor {i}/{len(wl.sizes)}")
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log(f"inputs resident in {time.perf_counter() - t0:.1f} s; "
+        f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
+
+    h = synth.HYPER
+    hy = dict(fmt_m=wl.fmt_m, fmt_v=wl.fmt_v, lr=h["lr"], beta1=h["b1"], beta2=h["b2"],
+              eps=h["eps"], weight_decay=h["wd"])
+    st.plan()
+    step = h["step"]
+    for _ in range(args.warmup):
+        st.step(step=step, **hy)
+        step += 1
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        st.step(step=step, **hy)
+        step += 1
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.float32, device=dev)  # 4 GiB read, 4 GiB written
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        log("copy calibration: 4 GiB fp32 copy done")
+
+    n = wl.n_params
+    bpp = wl.bytes_per_param()
+    launch_bytes = bpp * n
+    achieved = launch_bytes / (ms * 1e-3) / 1e9
+    traffic = load_traffic(args.workload, launch_bytes)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl)
+        log(f"cpu baseline {cpu['value']:.3e} params/s ({cpu['seconds']:.1f} s)")
+        cpu.pop("seconds")
+
+    out = {
+        "metric": "params/s of fused FP8-state AdamW step; achieved HBM GB/s vs 8 TB/s peak",
+        "value": n / (ms * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "n_params": n,
+            "tensors": len(wl.sizes),
+            "group": G,
+            "fmt_m": "E4M3", "fmt_v": "E5M2" if wl.fmt_v == 1 else "E4M3",
+            "bytes_per_param": bpp,
+            "launches_per_step": 1,
+            "hyper": {k: v for k, v in h.items()},
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
