@@ -10,18 +10,21 @@
 //
 // Design (MI355X / CDNA4):
 //   * one wavefront owns a tile of 1024 consecutive elements of one tensor;
-//     each lane owns 16 consecutive elements, so every stream moves with
-//     128-bit loads/stores (fp32 4x16 B, bf16 2x16 B, each FP8 stream 16 B);
+//     each lane owns 16 consecutive elements (128-bit loads and stores of
+//     every stream);
 //   * a group of G elements spans G/16 lanes of one wave; group statistics
-//     are butterfly reductions across those lanes, no LDS round trip;
+//     are DPP butterfly reductions across those lanes, no LDS round trip;
 //   * moments are dequantized, updated and reduced in fp64 (CDNA4 runs fp64
 //     FMA at the fp32 rate): the group's k and s are ill-conditioned in its
 //     smallest |m'|, usually a near-cancellation of b1*m and (1-b1)*g, so the
 //     per-element chain carries 53 bits;
+//   * the per-group scalar work (k, s, the dequantization constants) runs
+//     once per lane pair: the even lane of a pair does the first moment, the
+//     odd lane the second, and the pair swaps results through DPP;
 //   * requantization runs in fp32 with the native v_log_f32 / v_exp_f32 and
 //     the hardware OCP FP8 converts; an element whose expanded value lies
-//     within a relative window of an FP8 rounding midpoint is redone exactly
-//     in fp64 with a software encoder, so codes are the exact rounding;
+//     within a relative window of an FP8 rounding midpoint is decided exactly
+//     in fp64 by comparing |x| with the group's threshold for that midpoint;
 //   * the AdamW update itself (master weights, bf16 copy) runs in fp32;
 //   * the multi-tensor kernel walks a descriptor table of a whole parameter
 //     list in one launch; tiles never span tensors.
@@ -39,6 +42,12 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) float gfloat;
+typedef __attribute__((address_space(1))) uint16_t gu16;
+typedef __attribute__((address_space(1))) uint8_t gu8;
+typedef __attribute__((address_space(1))) double gf64;
+typedef __attribute__((address_space(1))) f32x4 gf32x4;
+typedef __attribute__((address_space(1))) u32x4 gu32x4;
 
 constexpr int kWave = 64;
 constexpr int kLaneElems = 16;
@@ -47,10 +56,16 @@ constexpr int kBlock = 256;                // 4 wavefronts
 constexpr int kWavesPerBlock = kBlock / kWave;
 
 // Relative half-width of the window around an FP8 rounding midpoint inside
-// which the fp32 fast path defers to the exact fp64 path. The fast path's
-// error is a few 1e-6 relative at most (log/exp of arguments up to 32 in
-// magnitude); 2^-15 leaves an order of magnitude of margin.
+// which the fp32 fast path defers to the exact fp64 decision. The fast path's
+// error stays below about 7e-6 relative (native log2/exp2 of arguments up to
+// 32 in magnitude and three fp32 roundings of |x| / amax amplified by k);
+// 2^-15 = 3.05e-5 keeps a margin of more than 4x.
 constexpr float kAmbiguity = 0x1p-15f;
+
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gp(T* p) {
+    return (__attribute__((address_space(1))) T*)p;
+}
 
 // ------------------------------------------------------------------ formats
 
@@ -87,30 +102,42 @@ struct Fmt<COAT_FMT_E5M2> {
     __device__ static bool is_inf(int c) { return c == 0x7C; }
 };
 
+// Per-lane format constants, for code that serves both moments at once.
+struct FmtRT {
+    double fpmax, log2_fpmax, log2_rf;
+    float fpmax_f, log2_fpmax_f;
+};
+template <int F>
+__device__ __forceinline__ FmtRT fmt_rt() {
+    using T = Fmt<F>;
+    return FmtRT{T::FPMAX, T::LOG2_FPMAX, T::LOG2_RF, T::FPMAX_F, T::LOG2_FPMAX_F};
+}
+
 // ------------------------------------------------------------------ fp64 math
 //
-// exp2: u = n + f with n = rint(u), |f| <= 1/2, and 2^f = exp(f ln 2) from its
-// Taylor series sum (ln 2)^i f^i / i!. Degree 13 truncates below 2^-57 on
-// |f| <= 1/2; the per-element path uses degree 11 (below 2^-47), which keeps
-// the dequantized moments far inside what the group statistics need.
+// exp2: u = n + f with n = rint(u), |f| <= 1/2, and 2^f = exp(f ln 2). The
+// per-group routine uses its Taylor series sum (ln 2)^i f^i / i! to degree 13
+// (truncation below 2^-57 on |f| <= 1/2). The per-element routine uses the
+// degree-9 polynomial interpolating 2^f at the ten Chebyshev nodes of
+// [-1/2, 1/2] (relative error below 2^-45.6), which keeps the dequantized
+// moments far inside what the group statistics need.
 // log2: x = m 2^e with m in [sqrt(1/2), sqrt(2)), u = (m-1)/(m+1), and
 // ln m = 2 atanh(u) = 2 sum u^(2j+1) / (2j+1); |u| <= 0.1716, so 12 terms
-// reach 2^-56. Coefficients are (ln 2)^i / i! and 2 log2(e) / (2j+1) rounded
-// to fp64.
+// reach 2^-56. Quotients and reciprocals use the hardware reciprocal estimate
+// refined by Newton steps. Coefficients are (ln 2)^i / i! and
+// 2 log2(e) / (2j+1) rounded to fp64.
 
-__device__ __forceinline__ double exp2_poly11(double f) {
-    double p = 0x1.e8cac7351bb25p-32;
-    p = __builtin_fma(p, f, 0x1.e4cf5158b8ecap-28);
-    p = __builtin_fma(p, f, 0x1.b5253d395e7c4p-24);
-    p = __builtin_fma(p, f, 0x1.62c0223a5c824p-20);
-    p = __builtin_fma(p, f, 0x1.ffcbfc588b0c7p-17);
-    p = __builtin_fma(p, f, 0x1.430912f86c787p-13);
-    p = __builtin_fma(p, f, 0x1.5d87fe78a6731p-10);
-    p = __builtin_fma(p, f, 0x1.3b2ab6fba4e77p-7);
-    p = __builtin_fma(p, f, 0x1.c6b08d704a0c0p-5);
-    p = __builtin_fma(p, f, 0x1.ebfbdff82c58fp-3);
-    p = __builtin_fma(p, f, 0x1.62e42fefa39efp-1);
-    p = __builtin_fma(p, f, 1.0);
+__device__ __forceinline__ double exp2_poly9(double f) {
+    double p = 0x1.b6571de2f2351p-24;
+    p = __builtin_fma(p, f, 0x1.63ef969a64d3cp-20);
+    p = __builtin_fma(p, f, 0x1.ffcb76789860fp-17);
+    p = __builtin_fma(p, f, 0x1.43088e257f341p-13);
+    p = __builtin_fma(p, f, 0x1.5d87fe908f88ap-10);
+    p = __builtin_fma(p, f, 0x1.3b2ab72b175eep-7);
+    p = __builtin_fma(p, f, 0x1.c6b08d7044119p-5);
+    p = __builtin_fma(p, f, 0x1.ebfbdff8149f2p-3);
+    p = __builtin_fma(p, f, 0x1.62e42fefa39f7p-1);
+    p = __builtin_fma(p, f, 0x1.000000000003dp+0);
     return p;
 }
 
@@ -140,11 +167,39 @@ __device__ __forceinline__ int cvt_i32_sat(double x) {
     return r;
 }
 
+// Plain fp64 max / min (v_max_f64, v_min_f64) of values that are never
+// signalling NaNs, without the quieting the IEEE mode would otherwise add.
+__device__ __forceinline__ double vmax(double a, double b) {
+    double r;
+    asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ double vmin(double a, double b) {
+    double r;
+    asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // 2^u for any u (NaN -> NaN, huge -> 0 / Inf).
 __device__ __forceinline__ double exp2_full(double u) {
     double n = __builtin_rint(u);
     double f = u - n;
     return __builtin_amdgcn_ldexp(exp2_poly13(f), cvt_i32_sat(n));
+}
+
+// 1/b for finite normal b: hardware estimate plus two Newton steps.
+__device__ __forceinline__ double rcp_f64(double b) {
+    double r = __builtin_amdgcn_rcp(b);
+    r = __builtin_fma(__builtin_fma(-b, r, 1.0), r, r);
+    r = __builtin_fma(__builtin_fma(-b, r, 1.0), r, r);
+    return r;
+}
+
+// a/b for finite normal b, within an ulp.
+__device__ __forceinline__ double div_f64(double a, double b) {
+    const double r = rcp_f64(b);
+    const double q = a * r;
+    return __builtin_fma(__builtin_fma(-b, q, a), r, q);
 }
 
 // log2(x) for finite x > 0 (normal or subnormal).
@@ -155,8 +210,8 @@ __device__ __forceinline__ double log2_full(double x) {
         m = m * 2.0;
         e -= 1;
     }
-    double u = (m - 1.0) / (m + 1.0);
-    double w = u * u;
+    const double u = div_f64(m - 1.0, m + 1.0);
+    const double w = u * u;
     double p = 0x1.00ecd7e080215p-3;
     p = __builtin_fma(p, w, 0x1.1964ec6fc9491p-3);
     p = __builtin_fma(p, w, 0x1.3703c1f4d0ffep-3);
@@ -177,6 +232,59 @@ __device__ __forceinline__ float next_up(float x) {  // x >= 0 finite
 }
 __device__ __forceinline__ float next_down(float x) {  // x > 0 finite
     return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) - 1u);
+}
+
+// ------------------------------------------------------------------ cross-lane
+
+// Value of lane (lane ^ 1), (lane ^ 2), ... via DPP within a row of 16.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = dpp32<CTRL>((uint32_t)b), hi = dpp32<CTRL>((uint32_t)(b >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within 16
+
+__device__ __forceinline__ double xlane64(double v, int d) {
+    switch (d) {
+        case 1: return dpp64<kDppXor1>(v);
+        case 2: return dpp64<kDppXor2>(v);
+        case 4: return dpp64<kDppHalfMirror>(v);
+        case 8: return dpp64<kDppMirror>(v);
+        default: return __shfl_xor(v, d, kWave);
+    }
+}
+__device__ __forceinline__ uint32_t xlane32(uint32_t v, int d) {
+    switch (d) {
+        case 1: return dpp32<kDppXor1>(v);
+        case 2: return dpp32<kDppXor2>(v);
+        case 4: return dpp32<kDppHalfMirror>(v);
+        case 8: return dpp32<kDppMirror>(v);
+        default: return (uint32_t)__shfl_xor((int)v, d, kWave);
+    }
+}
+
+// All-reduce over the `lanes` lanes (a power of two, aligned) owning a group.
+// After the first steps the sub-blocks agree, so the mirror permutations pair
+// every lane with one of the other half, as an xor would.
+__device__ __forceinline__ double group_max(double v, int lanes) {
+    for (int d = 1; d < lanes; d <<= 1) v = vmax(v, xlane64(v, d));
+    return v;
+}
+__device__ __forceinline__ double group_min(double v, int lanes) {
+    for (int d = 1; d < lanes; d <<= 1) v = vmin(v, xlane64(v, d));
+    return v;
+}
+__device__ __forceinline__ uint32_t group_or(uint32_t v, int lanes) {
+    for (int d = 1; d < lanes; d <<= 1) v |= xlane32(v, d);
+    return v;
 }
 
 // ------------------------------------------------------------------ FP8 codec
@@ -204,34 +312,45 @@ __device__ __forceinline__ uint32_t cvt_pk(float a, float b, uint32_t old) {
         return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, HI);
 }
 
+// Exact value of a magnitude code (finite codes only).
+template <int F>
+__device__ double value_of(int c) {
+    using T = Fmt<F>;
+    const int e = c >> T::MB, m = c & ((1 << T::MB) - 1);
+    return e ? __builtin_amdgcn_ldexp(1.0 + (double)m / (double)(1 << T::MB), e - T::BIAS)
+             : __builtin_amdgcn_ldexp((double)m, T::EMIN - T::MB);
+}
+
 // Exact value of an FP8 code.
 template <int F>
 __device__ float decode_value(uint32_t code) {
     using T = Fmt<F>;
-    int c = code & 0x7F;
+    const int c = code & 0x7F;
     float mag;
-    if (T::is_nan(c)) {
-        mag = __builtin_nanf("");
-    } else if (T::is_inf(c)) {
-        mag = __builtin_inff();
-    } else {
-        int e = c >> T::MB, m = c & ((1 << T::MB) - 1);
-        mag = e ? __builtin_amdgcn_ldexpf(1.0f + (float)m / (float)(1 << T::MB), e - T::BIAS)
-                : __builtin_amdgcn_ldexpf((float)m, T::EMIN - T::MB);
-    }
+    if (T::is_nan(c)) mag = __builtin_nanf("");
+    else if (T::is_inf(c)) mag = __builtin_inff();
+    else mag = (float)value_of<F>(c);
     return (code & 0x80) ? -mag : mag;
 }
 
-// log2(value(c) / fpmax) for magnitude code c, the per-code constant of the
-// dequantization x = A 2^(LQ[c] / k). Zero maps to -1e300 and Inf to +1e300
-// so that the same arithmetic yields 0 and Inf; NaN codes map to NaN.
+// Per-block constant tables, one row per moment:
+//   lq[c]  = log2(value(c) / fpmax), the per-code constant of the
+//            dequantization x = A 2^(lq[c] / k); zero maps to -1e300 and Inf to
+//            +1e300 so that the same arithmetic yields 0 and Inf, NaN codes to NaN;
+//   lqm[c] = log2(midpoint(c, c+1) / fpmax), the per-code constant of the
+//            exact requantization threshold.
+struct ConstTables {
+    double lq[2][128];
+    double lqm[2][128];
+};
+
 template <int F>
 __device__ double lq_entry(int c) {
     using T = Fmt<F>;
     if (T::is_nan(c)) return __builtin_nan("");
     if (T::is_inf(c)) return 1e300;
     if (c == 0) return -1e300;
-    int e = c >> T::MB, m = c & ((1 << T::MB) - 1);
+    const int e = c >> T::MB, m = c & ((1 << T::MB) - 1);
     double ip, fl;
     if (e == 0) {  // subnormal: m * 2^(EMIN - MB)
         ip = (double)(T::EMIN - T::MB);
@@ -243,52 +362,74 @@ __device__ double lq_entry(int c) {
     return (ip - T::LOG2_FPMAX) + fl;
 }
 
+template <int F>
+__device__ double lqm_entry(int c) {
+    using T = Fmt<F>;
+    if (c >= T::TOP) return 0.0;
+    const double mid = 0.5 * (value_of<F>(c) + value_of<F>(c + 1));
+    const int e = __builtin_amdgcn_frexp_exp(mid);
+    return ((double)e - T::LOG2_FPMAX) + log2_full(__builtin_amdgcn_frexp_mant(mid));
+}
+
+template <int FM, int FV>
+__device__ __forceinline__ void fill_tables(ConstTables& ct) {
+    const int i = threadIdx.x;
+    if (i < 128) {
+        ct.lq[0][i] = lq_entry<FM>(i);
+        ct.lqm[0][i] = lqm_entry<FM>(i);
+    } else if (i < 256) {
+        ct.lq[1][i - 128] = lq_entry<FV>(i - 128);
+        ct.lqm[1][i - 128] = lqm_entry<FV>(i - 128);
+    }
+    __syncthreads();
+}
+
 // ------------------------------------------------------------------ group state
 
-// Dequantization constants of a stored group: x = A 2^(LQ[q] r) with
-// A = (s fpmax)^(1/k) (the group's previous amax) and r = 1/k.
+// Dequantization constants of a stored group: x = 2^(LQ[q] r + a) with
+// r = 1/k and a = log2((s fpmax)^(1/k)), the log2 of the group's previous
+// amax. A zero scale gives a = -1e300 (every finite code decodes to 0) and a
+// NaN scale a = NaN.
 struct OldGroup {
-    double A;
+    double a;
     double r;
 };
 
-template <int F>
-__device__ OldGroup old_group(double s, float k) {
-    using T = Fmt<F>;
+__device__ __forceinline__ OldGroup old_group(double s, float k, double log2_fpmax) {
     OldGroup g;
-    g.r = 1.0 / (double)k;
-    if (s > 0.0 && s < __builtin_inf()) {
-        g.A = exp2_full((log2_full(s) + T::LOG2_FPMAX) * g.r);
-    } else {
-        g.A = (s == 0.0) ? 0.0 : (s > 0.0 ? s : __builtin_nan(""));  // 0, Inf, NaN propagate
-    }
+    g.r = rcp_f64((double)k);
+    if (s > 0.0 && s < __builtin_inf()) g.a = (log2_full(s) + log2_fpmax) * g.r;
+    else g.a = (s == 0.0) ? -1e300 : __builtin_nan("");
     return g;
 }
 
 // Requantization constants of a group from its statistics.
 struct NewGroup {
     double s;      // stored scale
+    double amax;   // largest magnitude (exact path)
+    double r;      // 1 / k in fp64 (exact path)
     float k;       // stored exponent
     float ia;      // 1 / amax in fp32 (0 for an all-zero group)
-    double amax;   // for the exact path
-    bool poison;   // non-finite member: every code 0x7F
-    bool fast_ok;  // fp32 fast path is valid for every member
+    uint32_t flags;
 };
+// v_cmp_class mask: signalling/quiet NaN, -Inf, -0, +0, +Inf.
+constexpr int kClassZeroInfNan = 0x1 | 0x2 | 0x4 | 0x20 | 0x40 | 0x200;
+constexpr uint32_t kPoison = 1u;  // non-finite member: every code 0x7F
+constexpr uint32_t kSlow = 2u;    // fp32 fast path unsafe for this group: exact path for all
 
 // k = ln R_fp8 / ln(amax / amin) (= log2 R_fp8 / log2 R), k = 1 for an
 // all-zero or near-constant group or without expansion; then the range guard:
-// amax^k and amax^k / R_fp8 within [2^-1022, 2^1023].
-template <int F>
-__device__ NewGroup new_group(double amax, double amin, bool poison, bool expand) {
-    using T = Fmt<F>;
+// amax^k and amax^k / R_fp8 within [2^-1022, 2^1023]; s = amax^k / fpmax.
+__device__ NewGroup new_group(double amax, double amin, bool poison, bool expand, const FmtRT& F) {
     NewGroup g;
-    g.poison = poison;
     g.amax = amax;
-    g.fast_ok = true;
+    g.flags = 0;
+    g.r = 1.0;
     if (poison) {
         g.s = __builtin_nan("");
         g.k = 1.0f;
         g.ia = 0.0f;
+        g.flags = kPoison;
         return g;
     }
     if (amax == 0.0) {
@@ -297,14 +438,14 @@ __device__ NewGroup new_group(double amax, double amin, bool poison, bool expand
         g.ia = 0.0f;
         return g;
     }
-    double L = log2_full(amax);
+    const double L = log2_full(amax);
     float k = 1.0f;
-    double R = amax / amin;
-    if (expand && R > 1.000001) k = (float)(T::LOG2_RF / log2_full(R));
-    double lo = -1022.0 + T::LOG2_RF, hi = 1023.0;
-    double kL = (double)k * L;
+    const double R = div_f64(amax, amin);
+    if (expand && R > 1.000001) k = (float)(F.log2_rf * rcp_f64(log2_full(R)));
+    const double lo = -1022.0 + F.log2_rf, hi = 1023.0;
+    const double kL = (double)k * L;
     if (!(kL >= lo && kL <= hi)) {
-        double bound = (L < 0.0) ? lo / L : hi / L;
+        const double bound = (L < 0.0) ? lo / L : hi / L;
         float kk = (float)bound;
         if (kk > k) kk = k;
         while (kk > 0.0f && !((double)kk * L >= lo && (double)kk * L <= hi)) kk = next_down(kk);
@@ -313,47 +454,89 @@ __device__ NewGroup new_group(double amax, double amin, bool poison, bool expand
         k = kk;
     }
     g.k = k;
-    g.s = exp2_full((double)k * L - T::LOG2_FPMAX);
-    g.ia = (float)(1.0 / amax);
-    // The fp32 path needs every member and 1/amax normal in fp32 and t = |x|/amax
+    g.r = rcp_f64((double)k);
+    g.s = exp2_full((double)k * L - F.log2_fpmax);
+    g.ia = (float)rcp_f64(amax);
+    // The fp32 path needs every member and 1/amax normal in fp32 and |x| / amax
     // at least 2^-100 for nonzero members.
-    g.fast_ok = amax <= 0x1p126 && amin >= 0x1p-126 && R <= 0x1p100;
+    if (!(amax <= 0x1p126 && amin >= 0x1p-126 && R <= 0x1p100)) g.flags = kSlow;
     return g;
 }
 
-// Exact code of one element: fpmax (|x| / amax)^k rounded in fp64.
+// Swap the per-group results of a lane pair (lane ^ 1).
+__device__ __forceinline__ OldGroup swap_pair(const OldGroup& g) {
+    return OldGroup{dpp64<kDppXor1>(g.a), dpp64<kDppXor1>(g.r)};
+}
+__device__ __forceinline__ NewGroup swap_pair(const NewGroup& g) {
+    NewGroup o;
+    o.s = g.s;  // stored by the computing lane only
+    o.amax = dpp64<kDppXor1>(g.amax);
+    o.r = dpp64<kDppXor1>(g.r);
+    o.k = __builtin_bit_cast(float, dpp32<kDppXor1>(__builtin_bit_cast(uint32_t, g.k)));
+    o.ia = __builtin_bit_cast(float, dpp32<kDppXor1>(__builtin_bit_cast(uint32_t, g.ia)));
+    o.flags = dpp32<kDppXor1>(g.flags);
+    return o;
+}
+
+// Exact code of one element with magnitude |x| whose fast-path code is `lo`
+// (magnitude) and which lies near the midpoint between lo and lo + 1:
+// y = fpmax (|x| / amax)^k against that midpoint, ties to the even code. For
+// k = 1 the expanded value is formed as fpmax (|x| / amax) with IEEE
+// operations; otherwise |x| is compared with amax 2^(log2(mid / fpmax) / k).
+__device__ __forceinline__ uint32_t exact_mag(double ax, uint32_t lo, const NewGroup& g,
+                                              const double* lqm, double mid, const FmtRT& F) {
+    bool up;
+    bool tie;
+    if (g.k == 1.0f) {
+        const double y = F.fpmax * (ax / g.amax);
+        up = y > mid;
+        tie = y == mid;
+    } else {
+        const double thr = g.amax * exp2_full(lqm[lo] * g.r);
+        up = ax > thr;
+        tie = ax == thr;
+    }
+    if (tie) up = (lo & 1u) != 0;
+    return up ? lo + 1 : lo;
+}
+
+// Exact code of one element from scratch (groups outside the fp32 path's range
+// and the standalone quantizer's slow elements): y = fpmax (|x| / amax)^k in
+// fp64, formed as fpmax (|x| / amax) with IEEE operations when k = 1.
 template <int F>
-__device__ uint32_t exact_code(double x, const NewGroup& g) {
+__device__ uint32_t exact_code_full(double x, const NewGroup& g) {
     using T = Fmt<F>;
-    uint32_t sign = __builtin_signbit(x) ? 0x80u : 0u;
-    if (g.poison) return 0x7F;
-    double t = __builtin_fabs(x) / g.amax;
-    if (!(t > 0.0)) return sign;  // zero member or all-zero group
-    double y = exp2_full((double)g.k * log2_full(t) + T::LOG2_FPMAX);
+    const uint32_t sign = __builtin_signbit(x) ? 0x80u : 0u;
+    if (g.flags & kPoison) return 0x7Fu;
+    if (x == 0.0 || g.amax == 0.0) return sign;
+    const double t = __builtin_fabs(x) / g.amax;
+    const double y = (g.k == 1.0f) ? T::FPMAX * t
+                                   : exp2_full((double)g.k * log2_full(t) + T::LOG2_FPMAX);
     return sign | encode_mag_exact<F>(y);
 }
 
 // Fast requantization of 4 elements (fp32 copies xf) into one code word;
-// returns the word and sets `amb` to 0x80 in each byte whose code is within the
-// ambiguity window of a rounding midpoint.
+// `amb` gets 0x80 in each byte whose code is within the ambiguity window of a
+// rounding midpoint.
 template <int F>
 __device__ __forceinline__ uint32_t fast_codes4(const float* xf, const NewGroup& g, uint32_t& amb) {
     using T = Fmt<F>;
     float lo[4], hi[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float t = __builtin_fabsf(xf[i]) * g.ia;
-        float l = __builtin_amdgcn_logf(t);
-        float z = __builtin_fmaf(g.k, l, T::LOG2_FPMAX_F);
-        float y = __builtin_amdgcn_exp2f(z);
+        const float t = __builtin_fabsf(xf[i]) * g.ia;
+        const float l = __builtin_amdgcn_logf(t);
+        const float z = __builtin_fmaf(g.k, l, T::LOG2_FPMAX_F);
+        const float y = __builtin_amdgcn_exp2f(z);
         lo[i] = __builtin_copysignf(y * (1.0f - kAmbiguity), xf[i]);
-        hi[i] = __builtin_fminf(y * (1.0f + kAmbiguity), T::FPMAX_F);
+        // y <= fpmax (1 + 1e-5) here, far below the overflow midpoint, so no clamp
+        hi[i] = y * (1.0f + kAmbiguity);
     }
     uint32_t wl = cvt_pk<F, false>(lo[0], lo[1], 0u);
     wl = cvt_pk<F, true>(lo[2], lo[3], wl);
     uint32_t wh = cvt_pk<F, false>(hi[0], hi[1], 0u);
     wh = cvt_pk<F, true>(hi[2], hi[3], wh);
-    uint32_t d = (wl ^ wh) & 0x7F7F7F7Fu;
+    const uint32_t d = (wl ^ wh) & 0x7F7F7F7Fu;
     amb = (d + 0x7F7F7F7Fu) & 0x80808080u;
     return wl;
 }
@@ -384,64 +567,107 @@ struct TensorRef {
 };
 static_assert(sizeof(TensorRef) == sizeof(coat_tensor), "descriptor layout");
 
+// Dequantize byte i of code word w: 2^(LQ[c] r + a) with the code's sign.
+__device__ __forceinline__ double dequant_w(uint32_t w, int i, const OldGroup& og, const double* lq) {
+    const double u = __builtin_fma(lq[__builtin_amdgcn_ubfe(w, 8 * i, 7)], og.r, og.a);
+    const double n = __builtin_rint(u);
+    const double x = __builtin_amdgcn_ldexp(exp2_poly9(u - n), cvt_i32_sat(n));
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const uint32_t sign = (w << (24 - 8 * i)) & 0x80000000u;
+    return __builtin_bit_cast(double, b | ((uint64_t)sign << 32));
+}
 __device__ __forceinline__ double dequant(uint32_t code, const OldGroup& og, const double* lq) {
-    double u = lq[code & 0x7F] * og.r;
-    double n = __builtin_rint(u);
-    double p = exp2_poly11(u - n);
-    double x = __builtin_amdgcn_ldexp(p * og.A, cvt_i32_sat(n));
-    return (code & 0x80) ? -x : x;
+    return dequant_w(code, 0, og, lq);
 }
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int i) { return (w >> (8 * i)) & 0xFFu; }
-
-// Lane-group all-reduce over the G/16 lanes owning one group (butterfly).
-__device__ __forceinline__ double group_max(double v, int lanes) {
-    for (int d = 1; d < lanes; d <<= 1) v = __builtin_fmax(v, __shfl_xor(v, d, kWave));
-    return v;
-}
-__device__ __forceinline__ double group_min(double v, int lanes) {
-    for (int d = 1; d < lanes; d <<= 1) v = __builtin_fmin(v, __shfl_xor(v, d, kWave));
-    return v;
-}
-__device__ __forceinline__ int group_or(int v, int lanes) {
-    for (int d = 1; d < lanes; d <<= 1) v |= __shfl_xor(v, d, kWave);
-    return v;
-}
 
 __device__ __forceinline__ uint32_t select4(int i, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
     return i == 0 ? a0 : (i == 1 ? a1 : (i == 2 ? a2 : a3));
 }
 
+__device__ __forceinline__ double bf16_to_f64(uint32_t word, int half) {
+    return (double)__builtin_bit_cast(float, half ? (word & 0xFFFF0000u) : (word << 16));
+}
+
+// Exact decision for the elements whose fast code is flagged in `amb` (one
+// moment): the element's new moment is recomputed in fp64 exactly as in the
+// main pass, then rounded with the fp64 threshold (or from scratch for groups
+// outside the fp32 path's range). Loops until no lane has a flagged element.
+template <int F>
+__device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&codes)[4], const uint32_t (&old)[4],
+                                               const uint32_t (&gw)[8], const OldGroup& og, const NewGroup& ng,
+                                               const double* lq, const double* lqm, const FmtRT& F_,
+                                               double b, double cb, bool square) {
+    while (__any((amb[0] | amb[1] | amb[2] | amb[3]) != 0u)) {
+        if ((amb[0] | amb[1] | amb[2] | amb[3]) != 0u) {
+            const int wi = amb[0] ? 0 : (amb[1] ? 1 : (amb[2] ? 2 : 3));
+            const uint32_t aw = select4(wi, amb[0], amb[1], amb[2], amb[3]);
+            const int bi = __builtin_ctz(aw) >> 3;
+            const int e = 4 * wi + bi;
+            const uint32_t oldw = select4(wi, old[0], old[1], old[2], old[3]);
+            const uint32_t gword = (e >> 1) < 4 ? select4(e >> 1, gw[0], gw[1], gw[2], gw[3])
+                                                : select4((e >> 1) - 4, gw[4], gw[5], gw[6], gw[7]);
+            const double g = bf16_to_f64(gword, e & 1);
+            const double x = __builtin_fma(b, dequant_w(oldw >> (8 * bi), 0, og, lq), cb * (square ? g * g : g));
+            const uint32_t fastw = select4(wi, codes[0], codes[1], codes[2], codes[3]);
+            const uint32_t lo = byte_of(fastw, bi) & 0x7Fu;
+            uint32_t code;
+            if (ng.flags & kSlow) {
+                code = exact_code_full<F>(x, ng);
+            } else {
+                const double mid = 0.5 * (value_of<F>(lo) + value_of<F>(lo + 1));
+                code = (__builtin_signbit(x) ? 0x80u : 0u) | exact_mag(__builtin_fabs(x), lo, ng, lqm, mid, F_);
+            }
+            const uint32_t mask = ~(0xFFu << (8 * bi)), ins = code << (8 * bi);
+            const uint32_t clear = ~(0x80u << (8 * bi));
+            if (wi == 0) { codes[0] = (codes[0] & mask) | ins; amb[0] &= clear; }
+            if (wi == 1) { codes[1] = (codes[1] & mask) | ins; amb[1] &= clear; }
+            if (wi == 2) { codes[2] = (codes[2] & mask) | ins; amb[2] &= clear; }
+            if (wi == 3) { codes[3] = (codes[3] & mask) | ins; amb[3] &= clear; }
+        }
+    }
+}
+
 // One wavefront tile of the step: elements [tile*1024, tile*1024 + 1024) of t.
 template <int FM, int FV>
-__device__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
-                          const double* lq_m, const double* lq_v) {
+__device__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c, const ConstTables& ct) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
     const int64_t rem = t.n - e0;
     const int nvalid = rem <= 0 ? 0 : (rem >= kLaneElems ? kLaneElems : (int)rem);
-    const int lanes_per_group = 1 << (c.lg2_group - 4);
+    const int lpg = 1 << (c.lg2_group - 4);  // lanes per group
     const int64_t gidx = e0 >> c.lg2_group;
+    // The lane's group holds elements (possibly not in this lane): its state is
+    // loaded and stored even by lanes past the end, which take part in the
+    // pair's per-group work.
+    const bool gvalid = (gidx << c.lg2_group) < t.n;
+    const bool pair = lpg >= 2;              // per-group work split over a lane pair
+    const bool odd = (lane & 1) != 0;
+    const FmtRT fm = fmt_rt<FM>(), fv = fmt_rt<FV>();
+
+    gfloat* P = gp(t.p);
+    const gu16* Gr = gp(t.g);
+    gu8* MQ = gp(t.mq);
+    gu8* VQ = gp(t.vq);
 
     // ---- loads (zeros past the end contribute nothing to the group statistics)
     float p[16];
     uint32_t gw[8], mq[4], vq[4];
     if (nvalid == kLaneElems) {
-        const f32x4* pp = reinterpret_cast<const f32x4*>(t.p + e0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            f32x4 v = __builtin_nontemporal_load(pp + i);
+            const f32x4 v = reinterpret_cast<const gf32x4*>(P + e0)[i];
             p[4 * i] = v.x; p[4 * i + 1] = v.y; p[4 * i + 2] = v.z; p[4 * i + 3] = v.w;
         }
-        const u32x4* gp = reinterpret_cast<const u32x4*>(t.g + e0);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            u32x4 v = __builtin_nontemporal_load(gp + i);
+            const u32x4 v = reinterpret_cast<const gu32x4*>(Gr + e0)[i];
             gw[4 * i] = v.x; gw[4 * i + 1] = v.y; gw[4 * i + 2] = v.z; gw[4 * i + 3] = v.w;
         }
-        u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(t.mq + e0));
+        const u32x4 a = *reinterpret_cast<const gu32x4*>(MQ + e0);
         mq[0] = a.x; mq[1] = a.y; mq[2] = a.z; mq[3] = a.w;
-        u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(t.vq + e0));
+        const u32x4 b = *reinterpret_cast<const gu32x4*>(VQ + e0);
         vq[0] = b.x; vq[1] = b.y; vq[2] = b.z; vq[3] = b.w;
     } else {
 #pragma unroll
@@ -451,94 +677,148 @@ __device__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const bool in = i < nvalid;
-            p[i] = in ? t.p[e0 + i] : 0.0f;
-            gw[i >> 1] |= in ? (uint32_t)t.g[e0 + i] << (16 * (i & 1)) : 0u;
-            mq[i >> 2] |= in ? (uint32_t)t.mq[e0 + i] << (8 * (i & 3)) : 0u;
-            vq[i >> 2] |= in ? (uint32_t)t.vq[e0 + i] << (8 * (i & 3)) : 0u;
+            p[i] = in ? P[e0 + i] : 0.0f;
+            gw[i >> 1] |= in ? (uint32_t)Gr[e0 + i] << (16 * (i & 1)) : 0u;
+            mq[i >> 2] |= in ? (uint32_t)MQ[e0 + i] << (8 * (i & 3)) : 0u;
+            vq[i >> 2] |= in ? (uint32_t)VQ[e0 + i] << (8 * (i & 3)) : 0u;
         }
     }
 
-    // ---- stored group state
-    double sm = 0.0, sv = 0.0;
-    float km = 1.0f, kv = 1.0f;
-    if (nvalid > 0) {
-        sm = t.ms[gidx]; km = t.mk[gidx];
-        sv = t.vs[gidx]; kv = t.vk[gidx];
+    // ---- stored group state -> dequantization constants
+    OldGroup om, ov;
+    if (pair) {
+        double s = 0.0;
+        float k = 1.0f;
+        if (gvalid) {
+            s = odd ? gp(t.vs)[gidx] : gp(t.ms)[gidx];
+            k = odd ? gp(t.vk)[gidx] : gp(t.mk)[gidx];
+        }
+        const OldGroup mine = old_group(s, k, odd ? fv.log2_fpmax : fm.log2_fpmax);
+        const OldGroup other = swap_pair(mine);
+        om = odd ? other : mine;
+        ov = odd ? mine : other;
+    } else {
+        double sm = 0.0, sv = 0.0;
+        float km = 1.0f, kv = 1.0f;
+        if (nvalid > 0) {
+            sm = gp(t.ms)[gidx]; km = gp(t.mk)[gidx];
+            sv = gp(t.vs)[gidx]; kv = gp(t.vk)[gidx];
+        }
+        om = old_group(sm, km, fm.log2_fpmax);
+        ov = old_group(sv, kv, fv.log2_fpmax);
     }
-    const OldGroup om = old_group<FM>(sm, km);
-    const OldGroup ov = old_group<FV>(sv, kv);
 
     // ---- per element: dequantize, moments, statistics, AdamW update
+    const double* lq_m = ct.lq[0];
+    const double* lq_v = ct.lq[1];
     float xm[16], xv[16];
     double amax_m = 0.0, amin_m = __builtin_inf(), amax_v = 0.0, amin_v = __builtin_inf();
-    bool bad = false;
+    bool special = false;  // a zero, infinite or NaN moment: the statistics are redone exactly
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const double m0 = dequant(byte_of(mq[i >> 2], i & 3), om, lq_m);
-        const double v0 = dequant(byte_of(vq[i >> 2], i & 3), ov, lq_v);
-        const double g = (double)__builtin_bit_cast(float, ((gw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16);
+        const double m0 = dequant_w(mq[i >> 2], i & 3, om, lq_m);
+        const double v0 = dequant_w(vq[i >> 2], i & 3, ov, lq_v);
+        const double g = bf16_to_f64(gw[i >> 1], i & 1);
         const double m1 = __builtin_fma(c.b1, m0, c.c1 * g);
         const double v1 = __builtin_fma(c.b2, v0, c.c2 * (g * g));
-        const double am = __builtin_fabs(m1), av = __builtin_fabs(v1);
-        bad |= !(am < __builtin_inf()) | !(av < __builtin_inf());
-        amax_m = __builtin_fmax(amax_m, am);
-        amin_m = __builtin_fmin(amin_m, am == 0.0 ? __builtin_inf() : am);
-        amax_v = __builtin_fmax(amax_v, av);
-        amin_v = __builtin_fmin(amin_v, av == 0.0 ? __builtin_inf() : av);
+        special |= __builtin_amdgcn_class(m1, kClassZeroInfNan) | __builtin_amdgcn_class(v1, kClassZeroInfNan);
+        amax_m = vmax(amax_m, __builtin_fabs(m1));
+        amin_m = vmin(amin_m, __builtin_fabs(m1));
+        amax_v = vmax(amax_v, __builtin_fabs(v1));
+        amin_v = vmin(amin_v, __builtin_fabs(v1));
         xm[i] = (float)m1;
         xv[i] = (float)v1;
         const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(xv[i]), c.ib2, c.eps);
         const float upd = xm[i] * __builtin_amdgcn_rcpf(den);
         p[i] = __builtin_fmaf(-c.ssz, upd, p[i] * c.decay);
     }
+    bool bad = false;
+    if (__any(special)) {
+        // Rare: exact statistics with zeros excluded from the minimum and
+        // non-finite moments flagged.
+        amax_m = 0.0; amin_m = __builtin_inf(); amax_v = 0.0; amin_v = __builtin_inf();
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t wm = select4(i >> 2, mq[0], mq[1], mq[2], mq[3]);
+            const uint32_t wv = select4(i >> 2, vq[0], vq[1], vq[2], vq[3]);
+            const uint32_t gword = (i >> 1) < 4 ? select4(i >> 1, gw[0], gw[1], gw[2], gw[3])
+                                                : select4((i >> 1) - 4, gw[4], gw[5], gw[6], gw[7]);
+            const double g = bf16_to_f64(gword, i & 1);
+            const double m1 = __builtin_fma(c.b1, dequant_w(wm >> (8 * (i & 3)), 0, om, lq_m), c.c1 * g);
+            const double v1 = __builtin_fma(c.b2, dequant_w(wv >> (8 * (i & 3)), 0, ov, lq_v), c.c2 * (g * g));
+            const double am = __builtin_fabs(m1), av = __builtin_fabs(v1);
+            bad |= !(am < __builtin_inf()) | !(av < __builtin_inf());
+            amax_m = vmax(amax_m, am);
+            amin_m = vmin(amin_m, am == 0.0 ? __builtin_inf() : am);
+            amax_v = vmax(amax_v, av);
+            amin_v = vmin(amin_v, av == 0.0 ? __builtin_inf() : av);
+        }
+    }
 
     // ---- store the new master weights and the bf16 copy
     if (nvalid == kLaneElems) {
-        f32x4* pp = reinterpret_cast<f32x4*>(t.p + e0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_nontemporal_store(f32x4{p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]}, pp + i);
+            reinterpret_cast<gf32x4*>(P + e0)[i] = f32x4{p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]};
         if (t.w) {
             uint32_t wb[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                __bf16 lo = (__bf16)p[2 * i], hi = (__bf16)p[2 * i + 1];
+                const __bf16 lo = (__bf16)p[2 * i], hi = (__bf16)p[2 * i + 1];
                 wb[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
             }
-            u32x4* wp = reinterpret_cast<u32x4*>(t.w + e0);
-            __builtin_nontemporal_store(u32x4{wb[0], wb[1], wb[2], wb[3]}, wp);
-            __builtin_nontemporal_store(u32x4{wb[4], wb[5], wb[6], wb[7]}, wp + 1);
+            gu32x4* wp = reinterpret_cast<gu32x4*>(gp(t.w) + e0);
+            wp[0] = u32x4{wb[0], wb[1], wb[2], wb[3]};
+            wp[1] = u32x4{wb[4], wb[5], wb[6], wb[7]};
         }
     } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             if (i < nvalid) {
-                t.p[e0 + i] = p[i];
-                if (t.w) t.w[e0 + i] = __builtin_bit_cast(uint16_t, (__bf16)p[i]);
+                P[e0 + i] = p[i];
+                if (t.w) gp(t.w)[e0 + i] = __builtin_bit_cast(uint16_t, (__bf16)p[i]);
             }
         }
     }
 
     // ---- group statistics across the group's lanes
-    amax_m = group_max(amax_m, lanes_per_group);
-    amin_m = group_min(amin_m, lanes_per_group);
-    amax_v = group_max(amax_v, lanes_per_group);
-    amin_v = group_min(amin_v, lanes_per_group);
-    const bool poison = group_or(bad ? 1 : 0, lanes_per_group) != 0;
+    amax_m = group_max(amax_m, lpg);
+    amin_m = group_min(amin_m, lpg);
+    amax_v = group_max(amax_v, lpg);
+    amin_v = group_min(amin_v, lpg);
     // A non-finite grad poisons both moments' groups (m' and v' both become non-finite).
-    const NewGroup nm = new_group<FM>(amax_m, amin_m, poison, c.expand_m);
-    const NewGroup nv = new_group<FV>(amax_v, amin_v, poison, c.expand_v);
+    const bool poison = group_or(bad ? 1u : 0u, lpg) != 0u;
 
-    // ---- requantize: fast fp32 codes, exact redo of ambiguous elements
+    // ---- requantization constants (the lane pair splits the two moments)
+    NewGroup nm, nv;
+    if (pair) {
+        const NewGroup mine = new_group(odd ? amax_v : amax_m, odd ? amin_v : amin_m, poison,
+                                        odd ? c.expand_v : c.expand_m, odd ? fv : fm);
+        const NewGroup other = swap_pair(mine);
+        nm = odd ? other : mine;
+        nv = odd ? mine : other;
+        if (gvalid && (lane & (lpg - 1)) < 2) {
+            if (odd) { gp(t.vs)[gidx] = mine.s; gp(t.vk)[gidx] = mine.k; }
+            else { gp(t.ms)[gidx] = mine.s; gp(t.mk)[gidx] = mine.k; }
+        }
+    } else {
+        nm = new_group(amax_m, amin_m, poison, c.expand_m, fm);
+        nv = new_group(amax_v, amin_v, poison, c.expand_v, fv);
+        if (nvalid > 0) {
+            gp(t.ms)[gidx] = nm.s; gp(t.mk)[gidx] = nm.k;
+            gp(t.vs)[gidx] = nv.s; gp(t.vk)[gidx] = nv.k;
+        }
+    }
+
+    // ---- requantize: fast fp32 codes, exact decision near midpoints
     uint32_t cm[4], cv[4], am[4], av[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         cm[i] = fast_codes4<FM>(xm + 4 * i, nm, am[i]);
         cv[i] = fast_codes4<FV>(xv + 4 * i, nv, av[i]);
     }
-    if (!nm.fast_ok) { am[0] = am[1] = am[2] = am[3] = 0x80808080u; }
-    if (!nv.fast_ok) { av[0] = av[1] = av[2] = av[3] = 0x80808080u; }
+    if (nm.flags & kSlow) { am[0] = am[1] = am[2] = am[3] = 0x80808080u; }
+    if (nv.flags & kSlow) { av[0] = av[1] = av[2] = av[3] = 0x80808080u; }
     if (nvalid < kLaneElems) {  // never redo elements past the end
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -549,81 +829,26 @@ __device__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
             av[i] &= keep;
         }
     }
-    if (nm.poison) { am[0] = am[1] = am[2] = am[3] = 0u; }
-    if (nv.poison) { av[0] = av[1] = av[2] = av[3] = 0u; }
-    // Pack the 32 flags of this lane (bit 4*i+b: m element 4i+b; bit 16+...: v).
-    uint32_t pend = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            pend |= ((am[i] >> (8 * b + 7)) & 1u) << (4 * i + b);
-            pend |= ((av[i] >> (8 * b + 7)) & 1u) << (16 + 4 * i + b);
-        }
-    }
-    while (__any(pend != 0u)) {
-        if (pend != 0u) {
-            const int j = __builtin_ctz(pend);
-            pend &= pend - 1u;
-            const bool is_v = j >= 16;
-            const int e = j & 15, wi = e >> 2, bi = e & 3;
-            // Recompute this element's new moment exactly as above.
-            const uint32_t codeword = is_v ? select4(wi, vq[0], vq[1], vq[2], vq[3])
-                                           : select4(wi, mq[0], mq[1], mq[2], mq[3]);
-            const uint32_t gword = (e >> 1) < 4 ? select4(e >> 1, gw[0], gw[1], gw[2], gw[3])
-                                                : select4((e >> 1) - 4, gw[4], gw[5], gw[6], gw[7]);
-            const double g = (double)__builtin_bit_cast(float, ((gword >> (16 * (e & 1))) & 0xFFFFu) << 16);
-            uint32_t code;
-            if (is_v) {
-                const double v1 = __builtin_fma(c.b2, dequant(byte_of(codeword, bi), ov, lq_v), c.c2 * (g * g));
-                code = exact_code<FV>(v1, nv);
-            } else {
-                const double m1 = __builtin_fma(c.b1, dequant(byte_of(codeword, bi), om, lq_m), c.c1 * g);
-                code = exact_code<FM>(m1, nm);
-            }
-            const uint32_t mask = ~(0xFFu << (8 * bi));
-            const uint32_t ins = code << (8 * bi);
-            if (is_v) {
-                if (wi == 0) cv[0] = (cv[0] & mask) | ins;
-                if (wi == 1) cv[1] = (cv[1] & mask) | ins;
-                if (wi == 2) cv[2] = (cv[2] & mask) | ins;
-                if (wi == 3) cv[3] = (cv[3] & mask) | ins;
-            } else {
-                if (wi == 0) cm[0] = (cm[0] & mask) | ins;
-                if (wi == 1) cm[1] = (cm[1] & mask) | ins;
-                if (wi == 2) cm[2] = (cm[2] & mask) | ins;
-                if (wi == 3) cm[3] = (cm[3] & mask) | ins;
-            }
-        }
-    }
-    if (nm.poison) { cm[0] = cm[1] = cm[2] = cm[3] = 0x7F7F7F7Fu; }
-    if (nv.poison) { cv[0] = cv[1] = cv[2] = cv[3] = 0x7F7F7F7Fu; }
+    if (nm.flags & kPoison) { am[0] = am[1] = am[2] = am[3] = 0u; }
+    if (nv.flags & kPoison) { av[0] = av[1] = av[2] = av[3] = 0u; }
+    redo_ambiguous<FM>(am, cm, mq, gw, om, nm, lq_m, ct.lqm[0], fm, c.b1, c.c1, false);
+    redo_ambiguous<FV>(av, cv, vq, gw, ov, nv, lq_v, ct.lqm[1], fv, c.b2, c.c2, true);
+    if (nm.flags & kPoison) { cm[0] = cm[1] = cm[2] = cm[3] = 0x7F7F7F7Fu; }
+    if (nv.flags & kPoison) { cv[0] = cv[1] = cv[2] = cv[3] = 0x7F7F7F7Fu; }
 
-    // ---- store codes and group state
+    // ---- store codes
     if (nvalid == kLaneElems) {
-        __builtin_nontemporal_store(u32x4{cm[0], cm[1], cm[2], cm[3]}, reinterpret_cast<u32x4*>(t.mq + e0));
-        __builtin_nontemporal_store(u32x4{cv[0], cv[1], cv[2], cv[3]}, reinterpret_cast<u32x4*>(t.vq + e0));
+        *reinterpret_cast<gu32x4*>(MQ + e0) = u32x4{cm[0], cm[1], cm[2], cm[3]};
+        *reinterpret_cast<gu32x4*>(VQ + e0) = u32x4{cv[0], cv[1], cv[2], cv[3]};
     } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             if (i < nvalid) {
-                t.mq[e0 + i] = (uint8_t)byte_of(cm[i >> 2], i & 3);
-                t.vq[e0 + i] = (uint8_t)byte_of(cv[i >> 2], i & 3);
+                MQ[e0 + i] = (uint8_t)byte_of(cm[i >> 2], i & 3);
+                VQ[e0 + i] = (uint8_t)byte_of(cv[i >> 2], i & 3);
             }
         }
     }
-    if (nvalid > 0 && (lane & (lanes_per_group - 1)) == 0) {
-        t.ms[gidx] = nm.s; t.mk[gidx] = nm.k;
-        t.vs[gidx] = nv.s; t.vk[gidx] = nv.k;
-    }
-}
-
-template <int FM, int FV>
-__device__ __forceinline__ void fill_lq_tables(double* lq_m, double* lq_v) {
-    const int i = threadIdx.x;
-    if (i < 128) lq_m[i] = lq_entry<FM>(i);
-    else if (i < 256) lq_v[i - 128] = lq_entry<FV>(i - 128);
-    __syncthreads();
 }
 
 __device__ __forceinline__ int64_t wave_id() {
@@ -632,11 +857,11 @@ __device__ __forceinline__ int64_t wave_id() {
 
 template <int FM, int FV>
 __global__ __launch_bounds__(kBlock) void step_single_kernel(TensorRef t, StepConsts c) {
-    __shared__ double lq[2][128];
-    fill_lq_tables<FM, FV>(lq[0], lq[1]);
+    __shared__ ConstTables ct;
+    fill_tables<FM, FV>(ct);
     const int64_t tiles = (t.n + kTile - 1) / kTile;
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t tile = wave_id(); tile < tiles; tile += nw) step_tile<FM, FV>(t, tile, c, lq[0], lq[1]);
+    for (int64_t tile = wave_id(); tile < tiles; tile += nw) step_tile<FM, FV>(t, tile, c, ct);
 }
 
 // Multi-tensor: descriptors and the tile prefix (count + 1 entries) live in
@@ -646,14 +871,14 @@ template <int FM, int FV>
 __global__ __launch_bounds__(kBlock) void step_multi_kernel(const TensorRef* __restrict__ ts,
                                                             const int64_t* __restrict__ tile_begin,
                                                             int count, StepConsts c) {
-    __shared__ double lq[2][128];
-    fill_lq_tables<FM, FV>(lq[0], lq[1]);
+    __shared__ ConstTables ct;
+    fill_tables<FM, FV>(ct);
     const int64_t tiles = tile_begin[count];
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     int cur = 0;
     for (int64_t tile = wave_id(); tile < tiles; tile += nw) {
         while (tile >= tile_begin[cur + 1]) ++cur;
-        step_tile<FM, FV>(ts[cur], tile - tile_begin[cur], c, lq[0], lq[1]);
+        step_tile<FM, FV>(ts[cur], tile - tile_begin[cur], c, ct);
     }
 }
 
@@ -664,25 +889,29 @@ template <int F>
 __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restrict__ x, int64_t n,
                                                           int lg2_group, int expand, uint8_t* q,
                                                           double* s, float* k) {
+    __shared__ ConstTables ct;
+    fill_tables<F, F>(ct);
     const int64_t tiles = (n + kTile - 1) / kTile;
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int lane = threadIdx.x & (kWave - 1);
-    const int lanes_per_group = 1 << (lg2_group - 4);
+    const int lpg = 1 << (lg2_group - 4);
+    const FmtRT fr = fmt_rt<F>();
+    const gfloat* X = gp(x);
+    gu8* Q = gp(q);
     for (int64_t tile = wave_id(); tile < tiles; tile += nw) {
         const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
         const int64_t rem = n - e0;
         const int nvalid = rem <= 0 ? 0 : (rem >= kLaneElems ? kLaneElems : (int)rem);
         float xf[16];
         if (nvalid == kLaneElems) {
-            const f32x4* xp = reinterpret_cast<const f32x4*>(x + e0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                f32x4 v = __builtin_nontemporal_load(xp + i);
+                const f32x4 v = reinterpret_cast<const gf32x4*>(X + e0)[i];
                 xf[4 * i] = v.x; xf[4 * i + 1] = v.y; xf[4 * i + 2] = v.z; xf[4 * i + 3] = v.w;
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) xf[i] = i < nvalid ? x[e0 + i] : 0.0f;
+            for (int i = 0; i < 16; ++i) xf[i] = i < nvalid ? X[e0 + i] : 0.0f;
         }
         double amax = 0.0, amin = __builtin_inf();
         bool bad = false;
@@ -690,52 +919,63 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
         for (int i = 0; i < 16; ++i) {
             const double a = __builtin_fabs((double)xf[i]);
             bad |= !(a < __builtin_inf());
-            amax = __builtin_fmax(amax, a);
-            amin = __builtin_fmin(amin, a == 0.0 ? __builtin_inf() : a);
+            amax = vmax(amax, a);
+            amin = vmin(amin, a == 0.0 ? __builtin_inf() : a);
         }
-        amax = group_max(amax, lanes_per_group);
-        amin = group_min(amin, lanes_per_group);
-        const bool poison = group_or(bad ? 1 : 0, lanes_per_group) != 0;
-        const NewGroup ng = new_group<F>(amax, amin, poison, expand);
+        amax = group_max(amax, lpg);
+        amin = group_min(amin, lpg);
+        const bool poison = group_or(bad ? 1u : 0u, lpg) != 0u;
+        const NewGroup ng = new_group(amax, amin, poison, expand, fr);
         uint32_t cw[4], amb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) cw[i] = fast_codes4<F>(xf + 4 * i, ng, amb[i]);
-        uint32_t pend = 0;
+        if (ng.flags & kSlow) { amb[0] = amb[1] = amb[2] = amb[3] = 0x80808080u; }
+        if (nvalid < kLaneElems) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
+                uint32_t keep = 0;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) pend |= ((amb[i] >> (8 * b + 7)) & 1u) << (4 * i + b);
-        if (!ng.fast_ok) pend = 0xFFFFu;
-        if (nvalid < kLaneElems) pend &= (1u << nvalid) - 1u;
-        if (ng.poison) pend = 0;
-        while (__any(pend != 0u)) {
-            if (pend != 0u) {
-                const int e = __builtin_ctz(pend);
-                pend &= pend - 1u;
+                for (int b = 0; b < 4; ++b) keep |= (4 * i + b < nvalid) ? (0x80u << (8 * b)) : 0u;
+                amb[i] &= keep;
+            }
+        }
+        if (ng.flags & kPoison) { amb[0] = amb[1] = amb[2] = amb[3] = 0u; }
+        while (__any((amb[0] | amb[1] | amb[2] | amb[3]) != 0u)) {
+            if ((amb[0] | amb[1] | amb[2] | amb[3]) != 0u) {
+                const int wi = amb[0] ? 0 : (amb[1] ? 1 : (amb[2] ? 2 : 3));
+                const uint32_t aw = select4(wi, amb[0], amb[1], amb[2], amb[3]);
+                const int bi = __builtin_ctz(aw) >> 3;
+                const int e = 4 * wi + bi;
                 float xe = xf[0];
 #pragma unroll
                 for (int i = 1; i < 16; ++i) xe = (e == i) ? xf[i] : xe;
-                const uint32_t code = exact_code<F>((double)xe, ng);
-                const int wi = e >> 2, bi = e & 3;
+                const double xd = (double)xe;
+                const uint32_t lo = byte_of(select4(wi, cw[0], cw[1], cw[2], cw[3]), bi) & 0x7Fu;
+                const double mid = 0.5 * (value_of<F>(lo) + value_of<F>(lo + 1));
+                const uint32_t code = (ng.flags & kSlow)
+                                          ? exact_code_full<F>(xd, ng)
+                                          : ((__builtin_signbit(xd) ? 0x80u : 0u) |
+                                             exact_mag(__builtin_fabs(xd), lo, ng, ct.lqm[0], mid, fr));
                 const uint32_t mask = ~(0xFFu << (8 * bi)), ins = code << (8 * bi);
-                if (wi == 0) cw[0] = (cw[0] & mask) | ins;
-                if (wi == 1) cw[1] = (cw[1] & mask) | ins;
-                if (wi == 2) cw[2] = (cw[2] & mask) | ins;
-                if (wi == 3) cw[3] = (cw[3] & mask) | ins;
+                const uint32_t clear = ~(0x80u << (8 * bi));
+                if (wi == 0) { cw[0] = (cw[0] & mask) | ins; amb[0] &= clear; }
+                if (wi == 1) { cw[1] = (cw[1] & mask) | ins; amb[1] &= clear; }
+                if (wi == 2) { cw[2] = (cw[2] & mask) | ins; amb[2] &= clear; }
+                if (wi == 3) { cw[3] = (cw[3] & mask) | ins; amb[3] &= clear; }
             }
         }
-        if (ng.poison) { cw[0] = cw[1] = cw[2] = cw[3] = 0x7F7F7F7Fu; }
+        if (ng.flags & kPoison) { cw[0] = cw[1] = cw[2] = cw[3] = 0x7F7F7F7Fu; }
         if (nvalid == kLaneElems) {
-            __builtin_nontemporal_store(u32x4{cw[0], cw[1], cw[2], cw[3]}, reinterpret_cast<u32x4*>(q + e0));
+            *reinterpret_cast<gu32x4*>(Q + e0) = u32x4{cw[0], cw[1], cw[2], cw[3]};
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (i < nvalid) q[e0 + i] = (uint8_t)byte_of(cw[i >> 2], i & 3);
+                if (i < nvalid) Q[e0 + i] = (uint8_t)byte_of(cw[i >> 2], i & 3);
         }
-        if (nvalid > 0 && (lane & (lanes_per_group - 1)) == 0) {
+        if (nvalid > 0 && (lane & (lpg - 1)) == 0) {
             const int64_t gi = e0 >> lg2_group;
-            s[gi] = ng.s;
-            k[gi] = ng.k;
+            gp(s)[gi] = ng.s;
+            gp(k)[gi] = ng.k;
         }
     }
 }
@@ -745,33 +985,33 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __res
                                                             const double* __restrict__ s,
                                                             const float* __restrict__ k, int64_t n,
                                                             int lg2_group, float* __restrict__ x) {
-    __shared__ double lq[128];
-    if (threadIdx.x < 128) lq[threadIdx.x] = lq_entry<F>(threadIdx.x);
-    __syncthreads();
+    __shared__ ConstTables ct;
+    fill_tables<F, F>(ct);
     const int64_t tiles = (n + kTile - 1) / kTile;
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int lane = threadIdx.x & (kWave - 1);
+    const gu8* Q = gp(q);
+    gfloat* X = gp(x);
     for (int64_t tile = wave_id(); tile < tiles; tile += nw) {
         const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
         const int64_t rem = n - e0;
         const int nvalid = rem <= 0 ? 0 : (rem >= kLaneElems ? kLaneElems : (int)rem);
         if (nvalid == 0) continue;
         const int64_t gi = e0 >> lg2_group;
-        const OldGroup og = old_group<F>(s[gi], k[gi]);
+        const OldGroup og = old_group(gp(s)[gi], gp(k)[gi], Fmt<F>::LOG2_FPMAX);
         if (nvalid == kLaneElems) {
-            u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q + e0));
+            const u32x4 a = *reinterpret_cast<const gu32x4*>(Q + e0);
             const uint32_t w[4] = {a.x, a.y, a.z, a.w};
             float out[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) out[i] = (float)dequant(byte_of(w[i >> 2], i & 3), og, lq);
-            f32x4* xp = reinterpret_cast<f32x4*>(x + e0);
+            for (int i = 0; i < 16; ++i) out[i] = (float)dequant(byte_of(w[i >> 2], i & 3), og, ct.lq[0]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                __builtin_nontemporal_store(f32x4{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]}, xp + i);
+                reinterpret_cast<gf32x4*>(X + e0)[i] = f32x4{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (i < nvalid) x[e0 + i] = (float)dequant(q[e0 + i], og, lq);
+                if (i < nvalid) X[e0 + i] = (float)dequant(Q[e0 + i], og, ct.lq[0]);
         }
     }
 }
@@ -779,7 +1019,6 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __res
 template <int F>
 __global__ __launch_bounds__(kBlock) void encode_kernel(const float* __restrict__ y, int64_t n,
                                                         uint8_t* __restrict__ q) {
-    using T = Fmt<F>;
     const int64_t nw = (int64_t)gridDim.x * kBlock;
     for (int64_t i4 = (int64_t)blockIdx.x * kBlock + threadIdx.x; 4 * i4 < n; i4 += nw) {
         const int64_t e0 = 4 * i4;
@@ -790,8 +1029,8 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(const float* __restrict_
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const float a = __builtin_fabsf(v[b]);
-            lo[b] = __builtin_copysignf(__builtin_fminf(a * (1.0f - kAmbiguity), T::FPMAX_F), v[b]);
-            hi[b] = __builtin_fminf(a * (1.0f + kAmbiguity), T::FPMAX_F);
+            lo[b] = __builtin_copysignf(__builtin_fminf(a * (1.0f - kAmbiguity), Fmt<F>::FPMAX_F), v[b]);
+            hi[b] = __builtin_fminf(a * (1.0f + kAmbiguity), Fmt<F>::FPMAX_F);
         }
         uint32_t wl = cvt_pk<F, false>(lo[0], lo[1], 0u);
         wl = cvt_pk<F, true>(lo[2], lo[3], wl);
