@@ -81,6 +81,7 @@ struct Fmt<COAT_FMT_E4M3> {
     static constexpr double FPMAX = 448.0;
     static constexpr float FPMAX_F = 448.0f;
     static constexpr double LOG2_FPMAX = 0x1.19d5d9fd5010bp+3;  // log2(448)
+    static constexpr double LOG2_FPMAX_LO = 0x1.b332ac903a414p-52;  // its rounding error
     static constexpr float LOG2_FPMAX_F = 0x1.19d5dap+3f;
     static constexpr double LOG2_RF = 0x1.1ceaecfea8086p+4;     // log2(448 / 2^-9)
     __device__ static bool is_nan(int c) { return c == 0x7F; }
@@ -96,6 +97,7 @@ struct Fmt<COAT_FMT_E5M2> {
     static constexpr double FPMAX = 57344.0;
     static constexpr float FPMAX_F = 57344.0f;
     static constexpr double LOG2_FPMAX = 0x1.f9d5d9fd5010bp+3;  // log2(57344)
+    static constexpr double LOG2_FPMAX_LO = 0x1.b332ac903a414p-52;  // its rounding error
     static constexpr float LOG2_FPMAX_F = 0x1.f9d5dap+3f;
     static constexpr double LOG2_RF = 0x1.fceaecfea8086p+4;     // log2(57344 / 2^-16)
     __device__ static bool is_nan(int c) { return c > 0x7C; }
@@ -104,13 +106,13 @@ struct Fmt<COAT_FMT_E5M2> {
 
 // Per-lane format constants, for code that serves both moments at once.
 struct FmtRT {
-    double fpmax, log2_fpmax, log2_rf;
+    double fpmax, log2_fpmax, log2_fpmax_lo, log2_rf;
     float fpmax_f, log2_fpmax_f;
 };
 template <int F>
 __device__ __forceinline__ FmtRT fmt_rt() {
     using T = Fmt<F>;
-    return FmtRT{T::FPMAX, T::LOG2_FPMAX, T::LOG2_RF, T::FPMAX_F, T::LOG2_FPMAX_F};
+    return FmtRT{T::FPMAX, T::LOG2_FPMAX, T::LOG2_FPMAX_LO, T::LOG2_RF, T::FPMAX_F, T::LOG2_FPMAX_F};
 }
 
 // ------------------------------------------------------------------ fp64 math
@@ -118,26 +120,30 @@ __device__ __forceinline__ FmtRT fmt_rt() {
 // exp2: u = n + f with n = rint(u), |f| <= 1/2, and 2^f = exp(f ln 2). The
 // per-group routine uses its Taylor series sum (ln 2)^i f^i / i! to degree 13
 // (truncation below 2^-57 on |f| <= 1/2). The per-element routine uses the
-// degree-9 polynomial interpolating 2^f at the ten Chebyshev nodes of
-// [-1/2, 1/2] (relative error below 2^-45.6), which keeps the dequantized
-// moments far inside what the group statistics need.
+// degree-10 polynomial interpolating 2^f at the eleven Chebyshev nodes of
+// [-1/2, 1/2] (relative error below 2^-51.5). The smallest member of a group
+// is usually a near-cancellation b1*m + (1-b1)*g whose relative error is the
+// dequantization error amplified by |b1*m| / |m'| (1e8 and more in the tails
+// of a 13e9-element step), and k and s follow it, so the dequantized moments
+// are kept within a few 1e-15.
 // log2: x = m 2^e with m in [sqrt(1/2), sqrt(2)), u = (m-1)/(m+1), and
 // ln m = 2 atanh(u) = 2 sum u^(2j+1) / (2j+1); |u| <= 0.1716, so 12 terms
 // reach 2^-56. Quotients and reciprocals use the hardware reciprocal estimate
 // refined by Newton steps. Coefficients are (ln 2)^i / i! and
 // 2 log2(e) / (2j+1) rounded to fp64.
 
-__device__ __forceinline__ double exp2_poly9(double f) {
-    double p = 0x1.b6571de2f2351p-24;
-    p = __builtin_fma(p, f, 0x1.63ef969a64d3cp-20);
-    p = __builtin_fma(p, f, 0x1.ffcb76789860fp-17);
-    p = __builtin_fma(p, f, 0x1.43088e257f341p-13);
-    p = __builtin_fma(p, f, 0x1.5d87fe908f88ap-10);
-    p = __builtin_fma(p, f, 0x1.3b2ab72b175eep-7);
-    p = __builtin_fma(p, f, 0x1.c6b08d7044119p-5);
-    p = __builtin_fma(p, f, 0x1.ebfbdff8149f2p-3);
-    p = __builtin_fma(p, f, 0x1.62e42fefa39f7p-1);
-    p = __builtin_fma(p, f, 0x1.000000000003dp+0);
+__device__ __forceinline__ double exp2_poly10(double f) {
+    double p = 0x1.e6063f7217bc6p-28;
+    p = __builtin_fma(p, f, 0x1.b675bca4eeebbp-24);
+    p = __builtin_fma(p, f, 0x1.62bfd47773353p-20);
+    p = __builtin_fma(p, f, 0x1.ffcb54062e698p-17);
+    p = __builtin_fma(p, f, 0x1.430913096fd9fp-13);
+    p = __builtin_fma(p, f, 0x1.5d87fe9d7a584p-10);
+    p = __builtin_fma(p, f, 0x1.3b2ab6fba1ddap-7);
+    p = __builtin_fma(p, f, 0x1.c6b08d703ce49p-5);
+    p = __builtin_fma(p, f, 0x1.ebfbdff82c598p-3);
+    p = __builtin_fma(p, f, 0x1.62e42fefa3a19p-1);
+    p = __builtin_fma(p, f, 1.0);
     return p;
 }
 
@@ -202,8 +208,10 @@ __device__ __forceinline__ double div_f64(double a, double b) {
     return __builtin_fma(__builtin_fma(-b, q, a), r, q);
 }
 
-// log2(x) for finite x > 0 (normal or subnormal).
-__device__ __forceinline__ double log2_full(double x) {
+// log2(x) for finite x > 0 (normal or subnormal); also returns the rounding
+// error of the result in `lo` (hi + lo carries about 2^-104 relative of the
+// exponent part, within the polynomial's own error).
+__device__ __forceinline__ double log2_full_dd(double x, double& lo) {
     int e = __builtin_amdgcn_frexp_exp(x);
     double m = __builtin_amdgcn_frexp_mant(x);  // [0.5, 1)
     if (m < 0x1.6a09e667f3bcdp-1) {             // sqrt(1/2)
@@ -224,7 +232,15 @@ __device__ __forceinline__ double log2_full(double x) {
     p = __builtin_fma(p, w, 0x1.2776c50ef9bfep-1);
     p = __builtin_fma(p, w, 0x1.ec709dc3a03fdp-1);
     p = __builtin_fma(p, w, 0x1.71547652b82fep+1);
-    return __builtin_fma(u, p, (double)e);
+    const double ed = (double)e;
+    const double hi = __builtin_fma(u, p, ed);
+    lo = __builtin_fma(u, p, ed - hi);  // ed - hi is exact (|u p| <= 1/2)
+    return hi;
+}
+
+__device__ __forceinline__ double log2_full(double x) {
+    double lo;
+    return log2_full_dd(x, lo);
 }
 
 __device__ __forceinline__ float next_up(float x) {  // x >= 0 finite
@@ -388,18 +404,34 @@ __device__ __forceinline__ void fill_tables(ConstTables& ct) {
 
 // Dequantization constants of a stored group: x = 2^(LQ[q] r + a) with
 // r = 1/k and a = log2((s fpmax)^(1/k)), the log2 of the group's previous
-// amax. A zero scale gives a = -1e300 (every finite code decodes to 0) and a
-// NaN scale a = NaN.
+// amax, carried as a + a_lo (double-double) so that the exponent keeps its
+// accuracy for |x| far from 1. A zero scale gives a = -1e300 (every finite
+// code decodes to 0) and a NaN scale a = NaN.
 struct OldGroup {
     double a;
+    double a_lo;
     double r;
 };
 
-__device__ __forceinline__ OldGroup old_group(double s, float k, double log2_fpmax) {
+__device__ __forceinline__ OldGroup old_group(double s, float k, double log2_fpmax, double log2_fpmax_lo) {
     OldGroup g;
-    g.r = rcp_f64((double)k);
-    if (s > 0.0 && s < __builtin_inf()) g.a = (log2_full(s) + log2_fpmax) * g.r;
-    else g.a = (s == 0.0) ? -1e300 : __builtin_nan("");
+    const double kd = (double)k;
+    g.r = rcp_f64(kd);
+    g.a_lo = 0.0;
+    if (s > 0.0 && s < __builtin_inf()) {
+        double l_lo;
+        const double l = log2_full_dd(s, l_lo);
+        // (l + l_lo) + (log2_fpmax + log2_fpmax_lo), two-sum of the leading parts
+        const double t = l + log2_fpmax;
+        const double bb = t - l;
+        const double t_lo = ((l - (t - bb)) + (log2_fpmax - bb)) + (l_lo + log2_fpmax_lo);
+        // (t + t_lo) * (r + r_lo), r_lo the rounding error of 1/k
+        const double r_lo = __builtin_fma(-kd, g.r, 1.0) * g.r;
+        g.a = t * g.r;
+        g.a_lo = __builtin_fma(t, g.r, -g.a) + __builtin_fma(t, r_lo, t_lo * g.r);
+    } else {
+        g.a = (s == 0.0) ? -1e300 : __builtin_nan("");
+    }
     return g;
 }
 
@@ -465,7 +497,7 @@ __device__ NewGroup new_group(double amax, double amin, bool poison, bool expand
 
 // Swap the per-group results of a lane pair (lane ^ 1).
 __device__ __forceinline__ OldGroup swap_pair(const OldGroup& g) {
-    return OldGroup{dpp64<kDppXor1>(g.a), dpp64<kDppXor1>(g.r)};
+    return OldGroup{dpp64<kDppXor1>(g.a), dpp64<kDppXor1>(g.a_lo), dpp64<kDppXor1>(g.r)};
 }
 __device__ __forceinline__ NewGroup swap_pair(const NewGroup& g) {
     NewGroup o;
@@ -567,11 +599,11 @@ struct TensorRef {
 };
 static_assert(sizeof(TensorRef) == sizeof(coat_tensor), "descriptor layout");
 
-// Dequantize byte i of code word w: 2^(LQ[c] r + a) with the code's sign.
+// Dequantize byte i of code word w: 2^(LQ[c] r + a + a_lo) with the code's sign.
 __device__ __forceinline__ double dequant_w(uint32_t w, int i, const OldGroup& og, const double* lq) {
     const double u = __builtin_fma(lq[__builtin_amdgcn_ubfe(w, 8 * i, 7)], og.r, og.a);
     const double n = __builtin_rint(u);
-    const double x = __builtin_amdgcn_ldexp(exp2_poly9(u - n), cvt_i32_sat(n));
+    const double x = __builtin_amdgcn_ldexp(exp2_poly10((u - n) + og.a_lo), cvt_i32_sat(n));
     const uint64_t b = __builtin_bit_cast(uint64_t, x);
     const uint32_t sign = (w << (24 - 8 * i)) & 0x80000000u;
     return __builtin_bit_cast(double, b | ((uint64_t)sign << 32));
@@ -693,7 +725,8 @@ __device__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
             s = odd ? gp(t.vs)[gidx] : gp(t.ms)[gidx];
             k = odd ? gp(t.vk)[gidx] : gp(t.mk)[gidx];
         }
-        const OldGroup mine = old_group(s, k, odd ? fv.log2_fpmax : fm.log2_fpmax);
+        const OldGroup mine = old_group(s, k, odd ? fv.log2_fpmax : fm.log2_fpmax,
+                                        odd ? fv.log2_fpmax_lo : fm.log2_fpmax_lo);
         const OldGroup other = swap_pair(mine);
         om = odd ? other : mine;
         ov = odd ? mine : other;
@@ -704,8 +737,8 @@ __device__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
             sm = gp(t.ms)[gidx]; km = gp(t.mk)[gidx];
             sv = gp(t.vs)[gidx]; kv = gp(t.vk)[gidx];
         }
-        om = old_group(sm, km, fm.log2_fpmax);
-        ov = old_group(sv, kv, fv.log2_fpmax);
+        om = old_group(sm, km, fm.log2_fpmax, fm.log2_fpmax_lo);
+        ov = old_group(sv, kv, fv.log2_fpmax, fv.log2_fpmax_lo);
     }
 
     // ---- per element: dequantize, moments, statistics, AdamW update
@@ -998,7 +1031,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __res
         const int nvalid = rem <= 0 ? 0 : (rem >= kLaneElems ? kLaneElems : (int)rem);
         if (nvalid == 0) continue;
         const int64_t gi = e0 >> lg2_group;
-        const OldGroup og = old_group(gp(s)[gi], gp(k)[gi], Fmt<F>::LOG2_FPMAX);
+        const OldGroup og = old_group(gp(s)[gi], gp(k)[gi], Fmt<F>::LOG2_FPMAX, Fmt<F>::LOG2_FPMAX_LO);
         if (nvalid == kLaneElems) {
             const u32x4 a = *reinterpret_cast<const gu32x4*>(Q + e0);
             const uint32_t w[4] = {a.x, a.y, a.z, a.w};

@@ -1,0 +1,134 @@
+"""GPU parity at the full workload sizes, sampled, in the launch configuration
+bench.py times (one multi-tensor launch over the whole parameter list).
+
+Inputs are generated on the device with the seeded generator; the prior
+moments are quantized on the device for every group, then the parity sample's
+groups are overwritten with the oracle's own quantization of the same prior
+values, so that every input the oracle sees comes from the generator or the
+oracle. The sample (synth.parity_sample): every tensor's first and last group,
+every group of the first transformer block, and every 997th group.
+"""
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _parity import HYPER, bf16_bits, compare, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def coat():
+    import fp8_optimizer_state_amd as c
+    assert torch.cuda.is_available()
+    c.lib()
+    return c
+
+
+def gather(t: torch.Tensor, G: int, idx: torch.Tensor) -> np.ndarray:
+    """Host copy of the groups `idx` of a flat per-element tensor."""
+    return t.view(-1, G)[idx].reshape(-1).cpu().numpy()
+
+
+def build(coat, wl, dev, sample):
+    """Device state for the whole list; returns it with the host inputs of the sample."""
+    G = wl.group
+    st = coat.ParamListState(wl.sizes, G, device=dev)
+    host = []
+    for i, n in enumerate(wl.sizes):
+        t = st.tensor(i)
+        synth.params(n, wl.seed, i, device=dev, out=t.params)
+        synth.grads(n, wl.seed, i, device=dev, out=t.grads)
+        m, v = synth.prior_moments(n, G, wl.seed, i, device=dev)
+        coat.quantize(m, t.m_q, t.m_s, t.m_k, group=G, fmt=wl.fmt_m)
+        coat.quantize(v, t.v_q, t.v_s, t.v_k, group=G, fmt=wl.fmt_v)
+        idx = torch.tensor(sample[i][1], dtype=torch.long, device=dev)
+        host.append(dict(idx=idx,
+                         p=gather(t.params, G, idx),
+                         g=bf16_bits(t.grads.view(-1, G)[idx].reshape(-1).cpu()),
+                         m=gather(m, G, idx), v=gather(v, G, idx)))
+        del m, v
+    torch.cuda.synchronize()
+    return st, host
+
+
+def oracle_quantize_sample(host, wl, threads=16):
+    def one(h):
+        h["mq"], h["ms"], h["mk"] = oracle.quantize(h["m"], wl.group, wl.fmt_m)
+        h["vq"], h["vs"], h["vk"] = oracle.quantize(h["v"], wl.group, wl.fmt_v)
+        del h["m"], h["v"]
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, host))
+
+
+def overwrite_sample(st, host, G):
+    """Put the oracle's prior state into the device state for the sampled groups."""
+    for i, h in enumerate(host):
+        t = st.tensor(i)
+        idx = h["idx"]
+        for key, dst in (("mq", t.m_q), ("vq", t.v_q)):
+            dst.view(-1, G)[idx] = torch.from_numpy(h[key].reshape(-1, G)).to(dst.device)
+        for key, dst in (("ms", t.m_s), ("mk", t.m_k), ("vs", t.v_s), ("vk", t.v_k)):
+            dst[idx] = torch.from_numpy(h[key]).to(dst.device)
+    torch.cuda.synchronize()
+
+
+def read_sample(st, host, G):
+    out = []
+    for i, h in enumerate(host):
+        t = st.tensor(i)
+        idx = h["idx"]
+        out.append(dict(p=gather(t.params, G, idx),
+                        w=bf16_bits(t.params_bf16.view(-1, G)[idx].reshape(-1).cpu()),
+                        mq=gather(t.m_q, G, idx), vq=gather(t.v_q, G, idx),
+                        ms=t.m_s[idx].cpu().numpy(), mk=t.m_k[idx].cpu().numpy(),
+                        vs=t.v_s[idx].cpu().numpy(), vk=t.v_k[idx].cpu().numpy()))
+    return out
+
+
+def oracle_steps(host, wl, step, threads=16):
+    h = HYPER
+
+    def one(x):
+        return oracle.adamw_step(x["p"], x["g"], x["mq"], x["ms"], x["mk"], x["vq"], x["vs"], x["vk"],
+                                 wl.group, wl.fmt_m, wl.fmt_v, h["lr"], h["b1"], h["b2"], h["eps"],
+                                 h["wd"], step)
+
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(one, host))
+
+
+def concat(lst):
+    return {k: np.concatenate([d[k] for d in lst]) for k in lst[0]}
+
+
+@pytest.mark.parametrize("name", ["llama13b", "llama7b", "llama13b_g32"])
+def test_full_size_sampled(coat, name):
+    wl = synth.WORKLOADS[name]
+    dev = torch.device("cuda")
+    sample = synth.parity_sample(wl)
+    n_sample = sum(len(ix) for _, ix in sample) * wl.group
+    log(f"test_full_size_sampled {name}: {wl.n_params} params, sample {n_sample} params")
+    t0 = time.time()
+    st, host = build(coat, wl, dev, sample)
+    log(f"  inputs on device ({time.time() - t0:.1f} s)")
+    oracle_quantize_sample(host, wl)
+    overwrite_sample(st, host, wl.group)
+    log(f"  sample state from the oracle ({time.time() - t0:.1f} s)")
+    h = HYPER
+    st.step(fmt_m=wl.fmt_m, fmt_v=wl.fmt_v, lr=h["lr"], beta1=h["b1"], beta2=h["b2"], eps=h["eps"],
+            weight_decay=h["wd"], step=h["step"])
+    torch.cuda.synchronize()
+    got = read_sample(st, host, wl.group)
+    del st
+    torch.cuda.empty_cache()
+    log(f"  gpu step done ({time.time() - t0:.1f} s)")
+    ref = oracle_steps(host, wl, h["step"])
+    log(f"  oracle done ({time.time() - t0:.1f} s)")
+    met = compare(concat(got), concat(ref), name)
+    assert met["m_k_rel"] < 1e-6 and met["v_k_rel"] < 1e-6
