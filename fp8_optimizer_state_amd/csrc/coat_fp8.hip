@@ -185,6 +185,17 @@ __device__ __forceinline__ double vmin(double a, double b) {
     asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
     return r;
 }
+// max(a, |b|) and min(a, |b|) with the absolute value as a source modifier.
+__device__ __forceinline__ double vmax_abs(double a, double b) {
+    double r;
+    asm("v_max_f64 %0, %1, |%2|" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ double vmin_abs(double a, double b) {
+    double r;
+    asm("v_min_f64 %0, %1, |%2|" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 
 // 2^u for any u (NaN -> NaN, huge -> 0 / Inf).
 __device__ __forceinline__ double exp2_full(double u) {
@@ -350,13 +361,20 @@ __device__ float decode_value(uint32_t code) {
 }
 
 // Per-block constant tables, one row per moment:
-//   lq[c]  = log2(value(c) / fpmax), the per-code constant of the
-//            dequantization x = A 2^(lq[c] / k); zero maps to -1e300 and Inf to
-//            +1e300 so that the same arithmetic yields 0 and Inf, NaN codes to NaN;
+//   lqb[c] = for each of the 256 codes, lq = log2(value(c & 0x7F) / fpmax), the
+//            per-code constant of the dequantization |x| = A 2^(lq / k) (zero
+//            maps to -1e300 and Inf to +1e300 so that the same arithmetic yields
+//            0 and Inf, NaN codes to NaN), and b = the moment's decay with the
+//            code's sign (the step's first operation on the dequantized value
+//            is b x; the codec kernels use b = 1);
 //   lqm[c] = log2(midpoint(c, c+1) / fpmax), the per-code constant of the
 //            exact requantization threshold.
+struct alignas(16) LqEntry {
+    double lq;
+    double b;
+};
 struct ConstTables {
-    double lq[2][128];
+    LqEntry lqb[2][256];
     double lqm[2][128];
 };
 
@@ -387,16 +405,16 @@ __device__ double lqm_entry(int c) {
     return ((double)e - T::LOG2_FPMAX) + log2_full(__builtin_amdgcn_frexp_mant(mid));
 }
 
+// Filled by the block's 256 threads: thread i covers moment i >> 7, code i & 127
+// and its negative.
 template <int FM, int FV>
-__device__ __forceinline__ void fill_tables(ConstTables& ct) {
-    const int i = threadIdx.x;
-    if (i < 128) {
-        ct.lq[0][i] = lq_entry<FM>(i);
-        ct.lqm[0][i] = lqm_entry<FM>(i);
-    } else if (i < 256) {
-        ct.lq[1][i - 128] = lq_entry<FV>(i - 128);
-        ct.lqm[1][i - 128] = lqm_entry<FV>(i - 128);
-    }
+__device__ __forceinline__ void fill_tables(ConstTables& ct, double bm, double bv) {
+    const int f = threadIdx.x >> 7, c = threadIdx.x & 127;
+    const double lq = f ? lq_entry<FV>(c) : lq_entry<FM>(c);
+    const double b = f ? bv : bm;
+    ct.lqb[f][c] = LqEntry{lq, b};
+    ct.lqb[f][c | 128] = LqEntry{lq, -b};
+    ct.lqm[f][c] = f ? lqm_entry<FV>(c) : lqm_entry<FM>(c);
     __syncthreads();
 }
 
@@ -444,8 +462,6 @@ struct NewGroup {
     float ia;      // 1 / amax in fp32 (0 for an all-zero group)
     uint32_t flags;
 };
-// v_cmp_class mask: signalling/quiet NaN, -Inf, -0, +0, +Inf.
-constexpr int kClassZeroInfNan = 0x1 | 0x2 | 0x4 | 0x20 | 0x40 | 0x200;
 constexpr uint32_t kPoison = 1u;  // non-finite member: every code 0x7F
 constexpr uint32_t kSlow = 2u;    // fp32 fast path unsafe for this group: exact path for all
 
@@ -564,9 +580,11 @@ __device__ __forceinline__ uint32_t fast_codes4(const float* xf, const NewGroup&
         // y <= fpmax (1 + 1e-5) here, far below the overflow midpoint, so no clamp
         hi[i] = y * (1.0f + kAmbiguity);
     }
-    uint32_t wl = cvt_pk<F, false>(lo[0], lo[1], 0u);
+    // The second convert writes the high halves, so the first one's
+    // passthrough operand may be any register that dies there.
+    uint32_t wl = cvt_pk<F, false>(lo[0], lo[1], __builtin_bit_cast(uint32_t, lo[0]));
     wl = cvt_pk<F, true>(lo[2], lo[3], wl);
-    uint32_t wh = cvt_pk<F, false>(hi[0], hi[1], 0u);
+    uint32_t wh = cvt_pk<F, false>(hi[0], hi[1], __builtin_bit_cast(uint32_t, hi[0]));
     wh = cvt_pk<F, true>(hi[2], hi[3], wh);
     const uint32_t d = (wl ^ wh) & 0x7F7F7F7Fu;
     amb = (d + 0x7F7F7F7Fu) & 0x80808080u;
@@ -599,17 +617,16 @@ struct TensorRef {
 };
 static_assert(sizeof(TensorRef) == sizeof(coat_tensor), "descriptor layout");
 
-// Dequantize byte i of code word w: 2^(LQ[c] r + a + a_lo) with the code's sign.
-__device__ __forceinline__ double dequant_w(uint32_t w, int i, const OldGroup& og, const double* lq) {
-    const double u = __builtin_fma(lq[__builtin_amdgcn_ubfe(w, 8 * i, 7)], og.r, og.a);
+// Dequantize byte i of code word w: returns the magnitude
+// 2^(LQ[c] r + a + a_lo) and sets tb to the code's table factor (+/- b), so
+// that the signed value times b is tb * magnitude.
+__device__ __forceinline__ double dequant_mag(uint32_t w, int i, const OldGroup& og, const LqEntry* t,
+                                              double& tb) {
+    const LqEntry e = t[(w >> (8 * i)) & 0xFFu];
+    tb = e.b;
+    const double u = __builtin_fma(e.lq, og.r, og.a);
     const double n = __builtin_rint(u);
-    const double x = __builtin_amdgcn_ldexp(exp2_poly10((u - n) + og.a_lo), cvt_i32_sat(n));
-    const uint64_t b = __builtin_bit_cast(uint64_t, x);
-    const uint32_t sign = (w << (24 - 8 * i)) & 0x80000000u;
-    return __builtin_bit_cast(double, b | ((uint64_t)sign << 32));
-}
-__device__ __forceinline__ double dequant(uint32_t code, const OldGroup& og, const double* lq) {
-    return dequant_w(code, 0, og, lq);
+    return __builtin_amdgcn_ldexp(exp2_poly10((u - n) + og.a_lo), cvt_i32_sat(n));
 }
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int i) { return (w >> (8 * i)) & 0xFFu; }
@@ -629,8 +646,8 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t word, int half) {
 template <int F>
 __device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&codes)[4], const uint32_t (&old)[4],
                                                const uint32_t (&gw)[8], const OldGroup& og, const NewGroup& ng,
-                                               const double* lq, const double* lqm, const FmtRT& F_,
-                                               double b, double cb, bool square) {
+                                               const LqEntry* lq, const double* lqm, const FmtRT& F_,
+                                               double cb, bool square) {
     while (__any((amb[0] | amb[1] | amb[2] | amb[3]) != 0u)) {
         if ((amb[0] | amb[1] | amb[2] | amb[3]) != 0u) {
             const int wi = amb[0] ? 0 : (amb[1] ? 1 : (amb[2] ? 2 : 3));
@@ -641,7 +658,9 @@ __device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&co
             const uint32_t gword = (e >> 1) < 4 ? select4(e >> 1, gw[0], gw[1], gw[2], gw[3])
                                                 : select4((e >> 1) - 4, gw[4], gw[5], gw[6], gw[7]);
             const double g = bf16_to_f64(gword, e & 1);
-            const double x = __builtin_fma(b, dequant_w(oldw >> (8 * bi), 0, og, lq), cb * (square ? g * g : g));
+            double tb;
+            const double mag = dequant_mag(oldw >> (8 * bi), 0, og, lq, tb);
+            const double x = __builtin_fma(tb, mag, cb * (square ? g * g : g));
             const uint32_t fastw = select4(wi, codes[0], codes[1], codes[2], codes[3]);
             const uint32_t lo = byte_of(fastw, bi) & 0x7Fu;
             uint32_t code;
@@ -742,29 +761,34 @@ __device__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
     }
 
     // ---- per element: dequantize, moments, statistics, AdamW update
-    const double* lq_m = ct.lq[0];
-    const double* lq_v = ct.lq[1];
+    const LqEntry* lq_m = ct.lqb[0];
+    const LqEntry* lq_v = ct.lqb[1];
     float xm[16], xv[16];
     double amax_m = 0.0, amin_m = __builtin_inf(), amax_v = 0.0, amin_v = __builtin_inf();
-    bool special = false;  // a zero, infinite or NaN moment: the statistics are redone exactly
+    // sum of xm * xv: not finite if any moment is infinite or NaN (or beyond fp32)
+    float fin = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const double m0 = dequant_w(mq[i >> 2], i & 3, om, lq_m);
-        const double v0 = dequant_w(vq[i >> 2], i & 3, ov, lq_v);
+        double tbm, tbv;
+        const double m0 = dequant_mag(mq[i >> 2], i & 3, om, lq_m, tbm);
+        const double v0 = dequant_mag(vq[i >> 2], i & 3, ov, lq_v, tbv);
         const double g = bf16_to_f64(gw[i >> 1], i & 1);
-        const double m1 = __builtin_fma(c.b1, m0, c.c1 * g);
-        const double v1 = __builtin_fma(c.b2, v0, c.c2 * (g * g));
-        special |= __builtin_amdgcn_class(m1, kClassZeroInfNan) | __builtin_amdgcn_class(v1, kClassZeroInfNan);
-        amax_m = vmax(amax_m, __builtin_fabs(m1));
-        amin_m = vmin(amin_m, __builtin_fabs(m1));
-        amax_v = vmax(amax_v, __builtin_fabs(v1));
-        amin_v = vmin(amin_v, __builtin_fabs(v1));
+        const double m1 = __builtin_fma(tbm, m0, c.c1 * g);
+        const double v1 = __builtin_fma(tbv, v0, c.c2 * (g * g));
+        amax_m = vmax_abs(amax_m, m1);
+        amin_m = vmin_abs(amin_m, m1);
+        amax_v = vmax_abs(amax_v, v1);
+        amin_v = vmin_abs(amin_v, v1);
         xm[i] = (float)m1;
         xv[i] = (float)v1;
+        fin = __builtin_fmaf(xm[i], xv[i], fin);
         const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(xv[i]), c.ib2, c.eps);
         const float upd = xm[i] * __builtin_amdgcn_rcpf(den);
         p[i] = __builtin_fmaf(-c.ssz, upd, p[i] * c.decay);
     }
+    // A zero moment (the minimum is over nonzero members) or a non-finite one:
+    // the statistics are redone exactly.
+    const bool special = amin_m == 0.0 || amin_v == 0.0 || !(__builtin_fabsf(fin) <= 0x1.fffffep+127f);
     bool bad = false;
     if (__any(special)) {
         // Rare: exact statistics with zeros excluded from the minimum and
@@ -776,8 +800,11 @@ __device__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
             const uint32_t gword = (i >> 1) < 4 ? select4(i >> 1, gw[0], gw[1], gw[2], gw[3])
                                                 : select4((i >> 1) - 4, gw[4], gw[5], gw[6], gw[7]);
             const double g = bf16_to_f64(gword, i & 1);
-            const double m1 = __builtin_fma(c.b1, dequant_w(wm >> (8 * (i & 3)), 0, om, lq_m), c.c1 * g);
-            const double v1 = __builtin_fma(c.b2, dequant_w(wv >> (8 * (i & 3)), 0, ov, lq_v), c.c2 * (g * g));
+            double tbm, tbv;
+            const double m0 = dequant_mag(wm >> (8 * (i & 3)), 0, om, lq_m, tbm);
+            const double v0 = dequant_mag(wv >> (8 * (i & 3)), 0, ov, lq_v, tbv);
+            const double m1 = __builtin_fma(tbm, m0, c.c1 * g);
+            const double v1 = __builtin_fma(tbv, v0, c.c2 * (g * g));
             const double am = __builtin_fabs(m1), av = __builtin_fabs(v1);
             bad |= !(am < __builtin_inf()) | !(av < __builtin_inf());
             amax_m = vmax(amax_m, am);
@@ -864,8 +891,8 @@ __device__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
     }
     if (nm.flags & kPoison) { am[0] = am[1] = am[2] = am[3] = 0u; }
     if (nv.flags & kPoison) { av[0] = av[1] = av[2] = av[3] = 0u; }
-    redo_ambiguous<FM>(am, cm, mq, gw, om, nm, lq_m, ct.lqm[0], fm, c.b1, c.c1, false);
-    redo_ambiguous<FV>(av, cv, vq, gw, ov, nv, lq_v, ct.lqm[1], fv, c.b2, c.c2, true);
+    redo_ambiguous<FM>(am, cm, mq, gw, om, nm, lq_m, ct.lqm[0], fm, c.c1, false);
+    redo_ambiguous<FV>(av, cv, vq, gw, ov, nv, lq_v, ct.lqm[1], fv, c.c2, true);
     if (nm.flags & kPoison) { cm[0] = cm[1] = cm[2] = cm[3] = 0x7F7F7F7Fu; }
     if (nv.flags & kPoison) { cv[0] = cv[1] = cv[2] = cv[3] = 0x7F7F7F7Fu; }
 
@@ -891,7 +918,7 @@ __device__ __forceinline__ int64_t wave_id() {
 template <int FM, int FV>
 __global__ __launch_bounds__(kBlock) void step_single_kernel(TensorRef t, StepConsts c) {
     __shared__ ConstTables ct;
-    fill_tables<FM, FV>(ct);
+    fill_tables<FM, FV>(ct, c.b1, c.b2);
     const int64_t tiles = (t.n + kTile - 1) / kTile;
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     for (int64_t tile = wave_id(); tile < tiles; tile += nw) step_tile<FM, FV>(t, tile, c, ct);
@@ -905,7 +932,7 @@ __global__ __launch_bounds__(kBlock) void step_multi_kernel(const TensorRef* __r
                                                             const int64_t* __restrict__ tile_begin,
                                                             int count, StepConsts c) {
     __shared__ ConstTables ct;
-    fill_tables<FM, FV>(ct);
+    fill_tables<FM, FV>(ct, c.b1, c.b2);
     const int64_t tiles = tile_begin[count];
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     int cur = 0;
@@ -923,7 +950,7 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
                                                           int lg2_group, int expand, uint8_t* q,
                                                           double* s, float* k) {
     __shared__ ConstTables ct;
-    fill_tables<F, F>(ct);
+    fill_tables<F, F>(ct, 1.0, 1.0);
     const int64_t tiles = (n + kTile - 1) / kTile;
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1019,7 +1046,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __res
                                                             const float* __restrict__ k, int64_t n,
                                                             int lg2_group, float* __restrict__ x) {
     __shared__ ConstTables ct;
-    fill_tables<F, F>(ct);
+    fill_tables<F, F>(ct, 1.0, 1.0);
     const int64_t tiles = (n + kTile - 1) / kTile;
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1037,14 +1064,22 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __res
             const uint32_t w[4] = {a.x, a.y, a.z, a.w};
             float out[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) out[i] = (float)dequant(byte_of(w[i >> 2], i & 3), og, ct.lq[0]);
+            for (int i = 0; i < 16; ++i) {
+                double tb;
+                const double mag = dequant_mag(w[i >> 2], i & 3, og, ct.lqb[0], tb);
+                out[i] = (float)(tb * mag);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 reinterpret_cast<gf32x4*>(X + e0)[i] = f32x4{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (i < nvalid) X[e0 + i] = (float)dequant(Q[e0 + i], og, ct.lq[0]);
+                if (i < nvalid) {
+                    double tb;
+                    const double mag = dequant_mag(Q[e0 + i], 0, og, ct.lqb[0], tb);
+                    X[e0 + i] = (float)(tb * mag);
+                }
         }
     }
 }
