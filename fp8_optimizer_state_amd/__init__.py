@@ -44,7 +44,7 @@ class _Tensor(ctypes.Structure):
 
 class _Plan(ctypes.Structure):
     _fields_ = [("workspace", ctypes.c_void_p), ("count", ctypes.c_int32),
-                ("tiles", ctypes.c_int64), ("n_total", ctypes.c_int64)]
+                ("tiles", ctypes.c_int64), ("n_total", ctypes.c_int64), ("n_partial", ctypes.c_int32)]
 
 
 _lib = None

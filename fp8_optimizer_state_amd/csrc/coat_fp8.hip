@@ -366,16 +366,13 @@ __device__ float decode_value(uint32_t code) {
 //            maps to -1e300 and Inf to +1e300 so that the same arithmetic yields
 //            0 and Inf, NaN codes to NaN), and b = the moment's decay with the
 //            code's sign (the step's first operation on the dequantized value
-//            is b x; the codec kernels use b = 1);
-//   lqm[c] = log2(midpoint(c, c+1) / fpmax), the per-code constant of the
-//            exact requantization threshold.
+//            is b x; the codec kernels use b = 1).
 struct alignas(16) LqEntry {
     double lq;
     double b;
 };
 struct ConstTables {
     LqEntry lqb[2][256];
-    double lqm[2][128];
 };
 
 template <int F>
@@ -396,6 +393,8 @@ __device__ double lq_entry(int c) {
     return (ip - T::LOG2_FPMAX) + fl;
 }
 
+// log2(midpoint(c, c+1) / fpmax): the constant of the exact requantization
+// threshold between magnitude codes c and c + 1 (rare path, computed on use).
 template <int F>
 __device__ double lqm_entry(int c) {
     using T = Fmt<F>;
@@ -414,7 +413,6 @@ __device__ __forceinline__ void fill_tables(ConstTables& ct, double bm, double b
     const double b = f ? bv : bm;
     ct.lqb[f][c] = LqEntry{lq, b};
     ct.lqb[f][c | 128] = LqEntry{lq, -b};
-    ct.lqm[f][c] = f ? lqm_entry<FV>(c) : lqm_entry<FM>(c);
     __syncthreads();
 }
 
@@ -531,8 +529,9 @@ __device__ __forceinline__ NewGroup swap_pair(const NewGroup& g) {
 // y = fpmax (|x| / amax)^k against that midpoint, ties to the even code. For
 // k = 1 the expanded value is formed as fpmax (|x| / amax) with IEEE
 // operations; otherwise |x| is compared with amax 2^(log2(mid / fpmax) / k).
-__device__ __forceinline__ uint32_t exact_mag(double ax, uint32_t lo, const NewGroup& g,
-                                              const double* lqm, double mid, const FmtRT& F) {
+template <int FMT>
+__device__ __forceinline__ uint32_t exact_mag(double ax, uint32_t lo, const NewGroup& g, double mid,
+                                              const FmtRT& F) {
     bool up;
     bool tie;
     if (g.k == 1.0f) {
@@ -540,7 +539,7 @@ __device__ __forceinline__ uint32_t exact_mag(double ax, uint32_t lo, const NewG
         up = y > mid;
         tie = y == mid;
     } else {
-        const double thr = g.amax * exp2_full(lqm[lo] * g.r);
+        const double thr = g.amax * exp2_full(lqm_entry<FMT>((int)lo) * g.r);
         up = ax > thr;
         tie = ax == thr;
     }
@@ -646,7 +645,7 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t word, int half) {
 template <int F>
 __device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&codes)[4], const uint32_t (&old)[4],
                                                const uint32_t (&gw)[8], const OldGroup& og, const NewGroup& ng,
-                                               const LqEntry* lq, const double* lqm, const FmtRT& F_,
+                                               const LqEntry* lq, const FmtRT& F_,
                                                double cb, bool square) {
     while (__any((amb[0] | amb[1] | amb[2] | amb[3]) != 0u)) {
         if ((amb[0] | amb[1] | amb[2] | amb[3]) != 0u) {
@@ -668,7 +667,7 @@ __device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&co
                 code = exact_code_full<F>(x, ng);
             } else {
                 const double mid = 0.5 * (value_of<F>(lo) + value_of<F>(lo + 1));
-                code = (__builtin_signbit(x) ? 0x80u : 0u) | exact_mag(__builtin_fabs(x), lo, ng, lqm, mid, F_);
+                code = (__builtin_signbit(x) ? 0x80u : 0u) | exact_mag<F>(__builtin_fabs(x), lo, ng, mid, F_);
             }
             const uint32_t mask = ~(0xFFu << (8 * bi)), ins = code << (8 * bi);
             const uint32_t clear = ~(0x80u << (8 * bi));
@@ -680,84 +679,146 @@ __device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&co
     }
 }
 
-// One wavefront tile of the step: elements [tile*1024, tile*1024 + 1024) of t.
-template <int FM, int FV>
-__device__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c, const ConstTables& ct) {
+// A wave-uniform copy of a pointer, held in scalar registers (so that a
+// per-lane choice between two such pointers needs no vector load).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+// Inputs of one wavefront tile.
+struct TileIn {
+    float p[16];
+    uint32_t gw[8], mq[4], vq[4];
+    double s0, s1;  // stored scales: the lane's moment (pair split) or m and v
+    float k0, k1;
+};
+
+// Synchronous loads of one tile for the general path (any group size, tiles
+// that end inside the tensor). Zeros past the end contribute nothing to the
+// group statistics. With the per-group work split over a lane pair, each lane
+// loads the stored state of one moment (even lane m, odd lane v) of its group,
+// also lanes past the end of the tensor, which take part in the pair's work.
+__device__ __forceinline__ void load_tile(const TensorRef& t, int64_t tile, int lg2_group, TileIn& in) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
     const int64_t rem = t.n - e0;
     const int nvalid = rem <= 0 ? 0 : (rem >= kLaneElems ? kLaneElems : (int)rem);
-    const int lpg = 1 << (c.lg2_group - 4);  // lanes per group
-    const int64_t gidx = e0 >> c.lg2_group;
-    // The lane's group holds elements (possibly not in this lane): its state is
-    // loaded and stored even by lanes past the end, which take part in the
-    // pair's per-group work.
-    const bool gvalid = (gidx << c.lg2_group) < t.n;
-    const bool pair = lpg >= 2;              // per-group work split over a lane pair
-    const bool odd = (lane & 1) != 0;
-    const FmtRT fm = fmt_rt<FM>(), fv = fmt_rt<FV>();
-
-    gfloat* P = gp(t.p);
+    const int64_t gidx = e0 >> lg2_group;
+    const gfloat* P = gp(t.p);
     const gu16* Gr = gp(t.g);
-    gu8* MQ = gp(t.mq);
-    gu8* VQ = gp(t.vq);
-
-    // ---- loads (zeros past the end contribute nothing to the group statistics)
-    float p[16];
-    uint32_t gw[8], mq[4], vq[4];
+    const gu8* MQ = gp(t.mq);
+    const gu8* VQ = gp(t.vq);
     if (nvalid == kLaneElems) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const f32x4 v = reinterpret_cast<const gf32x4*>(P + e0)[i];
-            p[4 * i] = v.x; p[4 * i + 1] = v.y; p[4 * i + 2] = v.z; p[4 * i + 3] = v.w;
+            in.p[4 * i] = v.x; in.p[4 * i + 1] = v.y; in.p[4 * i + 2] = v.z; in.p[4 * i + 3] = v.w;
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const u32x4 v = reinterpret_cast<const gu32x4*>(Gr + e0)[i];
-            gw[4 * i] = v.x; gw[4 * i + 1] = v.y; gw[4 * i + 2] = v.z; gw[4 * i + 3] = v.w;
+            in.gw[4 * i] = v.x; in.gw[4 * i + 1] = v.y; in.gw[4 * i + 2] = v.z; in.gw[4 * i + 3] = v.w;
         }
         const u32x4 a = *reinterpret_cast<const gu32x4*>(MQ + e0);
-        mq[0] = a.x; mq[1] = a.y; mq[2] = a.z; mq[3] = a.w;
+        in.mq[0] = a.x; in.mq[1] = a.y; in.mq[2] = a.z; in.mq[3] = a.w;
         const u32x4 b = *reinterpret_cast<const gu32x4*>(VQ + e0);
-        vq[0] = b.x; vq[1] = b.y; vq[2] = b.z; vq[3] = b.w;
+        in.vq[0] = b.x; in.vq[1] = b.y; in.vq[2] = b.z; in.vq[3] = b.w;
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) gw[i] = 0u;
+        for (int i = 0; i < 8; ++i) in.gw[i] = 0u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { mq[i] = 0u; vq[i] = 0u; }
+        for (int i = 0; i < 4; ++i) { in.mq[i] = 0u; in.vq[i] = 0u; }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const bool in = i < nvalid;
-            p[i] = in ? P[e0 + i] : 0.0f;
-            gw[i >> 1] |= in ? (uint32_t)Gr[e0 + i] << (16 * (i & 1)) : 0u;
-            mq[i >> 2] |= in ? (uint32_t)MQ[e0 + i] << (8 * (i & 3)) : 0u;
-            vq[i >> 2] |= in ? (uint32_t)VQ[e0 + i] << (8 * (i & 3)) : 0u;
+            const bool inb = i < nvalid;
+            in.p[i] = inb ? P[e0 + i] : 0.0f;
+            in.gw[i >> 1] |= inb ? (uint32_t)Gr[e0 + i] << (16 * (i & 1)) : 0u;
+            in.mq[i >> 2] |= inb ? (uint32_t)MQ[e0 + i] << (8 * (i & 3)) : 0u;
+            in.vq[i >> 2] |= inb ? (uint32_t)VQ[e0 + i] << (8 * (i & 3)) : 0u;
         }
     }
+    in.s0 = 0.0; in.s1 = 0.0; in.k0 = 1.0f; in.k1 = 1.0f;
+    if (lg2_group >= 5) {
+        if ((gidx << lg2_group) < t.n) {
+            const bool odd = (lane & 1) != 0;
+            in.s0 = odd ? gp(t.vs)[gidx] : gp(t.ms)[gidx];
+            in.k0 = odd ? gp(t.vk)[gidx] : gp(t.mk)[gidx];
+        }
+    } else if (nvalid > 0) {
+        in.s0 = gp(t.ms)[gidx]; in.k0 = gp(t.mk)[gidx];
+        in.s1 = gp(t.vs)[gidx]; in.k1 = gp(t.vk)[gidx];
+    }
+}
+
+// Loads of a tile that lies wholly inside its tensor, for group sizes whose
+// per-group work is split over lane pairs (even lane m, odd lane v).
+__device__ __forceinline__ void load_full_tile(const TensorRef& t, int64_t tile, int lg2_group, TileIn& in) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
+    const int64_t gidx = e0 >> lg2_group;
+    const bool odd = (lane & 1) != 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x4 v = reinterpret_cast<const gf32x4*>(gp(t.p) + e0)[i];
+        in.p[4 * i] = v.x; in.p[4 * i + 1] = v.y; in.p[4 * i + 2] = v.z; in.p[4 * i + 3] = v.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const u32x4 v = reinterpret_cast<const gu32x4*>(gp(t.g) + e0)[i];
+        in.gw[4 * i] = v.x; in.gw[4 * i + 1] = v.y; in.gw[4 * i + 2] = v.z; in.gw[4 * i + 3] = v.w;
+    }
+    const u32x4 a = *reinterpret_cast<const gu32x4*>(gp(t.mq) + e0);
+    in.mq[0] = a.x; in.mq[1] = a.y; in.mq[2] = a.z; in.mq[3] = a.w;
+    const u32x4 b = *reinterpret_cast<const gu32x4*>(gp(t.vq) + e0);
+    in.vq[0] = b.x; in.vq[1] = b.y; in.vq[2] = b.z; in.vq[3] = b.w;
+    in.s0 = gp(odd ? uniform_ptr(t.vs) : uniform_ptr(t.ms))[gidx];
+    in.k0 = gp(odd ? uniform_ptr(t.vk) : uniform_ptr(t.mk))[gidx];
+    in.s1 = 0.0;
+    in.k1 = 1.0f;
+}
+
+// One wavefront tile of the step: elements [tile*1024, tile*1024 + 1024) of t,
+// inputs in `in`. FULL: every element lies in the tensor and the group work is
+// split over lane pairs (group >= 32), so no lane needs a bounds check.
+template <int FM, int FV, bool FULL>
+__device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
+                                          const ConstTables& ct, TileIn& in) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
+    const int64_t rem = t.n - e0;
+    const int nvalid = FULL ? kLaneElems : (rem <= 0 ? 0 : (rem >= kLaneElems ? kLaneElems : (int)rem));
+    const int lpg = 1 << (c.lg2_group - 4);  // lanes per group
+    const int64_t gidx = e0 >> c.lg2_group;
+    // The lane's group holds elements (possibly not in this lane): its state is
+    // stored even by lanes past the end, which take part in the pair's work.
+    const bool gvalid = FULL || (gidx << c.lg2_group) < t.n;
+    const bool pair = FULL || lpg >= 2;      // per-group work split over a lane pair
+    const bool odd = (lane & 1) != 0;
+    const FmtRT fm = fmt_rt<FM>(), fv = fmt_rt<FV>();
+
+    gfloat* P = gp(t.p);
+    gu8* MQ = gp(t.mq);
+    gu8* VQ = gp(t.vq);
+    float (&p)[16] = in.p;
+    const uint32_t (&gw)[8] = in.gw;
+    const uint32_t (&mq)[4] = in.mq;
+    const uint32_t (&vq)[4] = in.vq;
 
     // ---- stored group state -> dequantization constants
     OldGroup om, ov;
     if (pair) {
-        double s = 0.0;
-        float k = 1.0f;
-        if (gvalid) {
-            s = odd ? gp(t.vs)[gidx] : gp(t.ms)[gidx];
-            k = odd ? gp(t.vk)[gidx] : gp(t.mk)[gidx];
-        }
-        const OldGroup mine = old_group(s, k, odd ? fv.log2_fpmax : fm.log2_fpmax,
+        const OldGroup mine = old_group(in.s0, in.k0, odd ? fv.log2_fpmax : fm.log2_fpmax,
                                         odd ? fv.log2_fpmax_lo : fm.log2_fpmax_lo);
         const OldGroup other = swap_pair(mine);
         om = odd ? other : mine;
         ov = odd ? mine : other;
     } else {
-        double sm = 0.0, sv = 0.0;
-        float km = 1.0f, kv = 1.0f;
-        if (nvalid > 0) {
-            sm = gp(t.ms)[gidx]; km = gp(t.mk)[gidx];
-            sv = gp(t.vs)[gidx]; kv = gp(t.vk)[gidx];
-        }
-        om = old_group(sm, km, fm.log2_fpmax, fm.log2_fpmax_lo);
-        ov = old_group(sv, kv, fv.log2_fpmax, fv.log2_fpmax_lo);
+        om = old_group(in.s0, in.k0, fm.log2_fpmax, fm.log2_fpmax_lo);
+        ov = old_group(in.s1, in.k1, fv.log2_fpmax, fv.log2_fpmax_lo);
     }
 
     // ---- per element: dequantize, moments, statistics, AdamW update
@@ -858,8 +919,10 @@ __device__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
         nm = odd ? other : mine;
         nv = odd ? mine : other;
         if (gvalid && (lane & (lpg - 1)) < 2) {
-            if (odd) { gp(t.vs)[gidx] = mine.s; gp(t.vk)[gidx] = mine.k; }
-            else { gp(t.ms)[gidx] = mine.s; gp(t.mk)[gidx] = mine.k; }
+            double* sp = odd ? uniform_ptr(t.vs) : uniform_ptr(t.ms);
+            float* kp = odd ? uniform_ptr(t.vk) : uniform_ptr(t.mk);
+            gp(sp)[gidx] = mine.s;
+            gp(kp)[gidx] = mine.k;
         }
     } else {
         nm = new_group(amax_m, amin_m, poison, c.expand_m, fm);
@@ -891,8 +954,10 @@ __device__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
     }
     if (nm.flags & kPoison) { am[0] = am[1] = am[2] = am[3] = 0u; }
     if (nv.flags & kPoison) { av[0] = av[1] = av[2] = av[3] = 0u; }
-    redo_ambiguous<FM>(am, cm, mq, gw, om, nm, lq_m, ct.lqm[0], fm, c.c1, false);
-    redo_ambiguous<FV>(av, cv, vq, gw, ov, nv, lq_v, ct.lqm[1], fv, c.c2, true);
+    if (__any((am[0] | am[1] | am[2] | am[3] | av[0] | av[1] | av[2] | av[3]) != 0u)) {
+        redo_ambiguous<FM>(am, cm, mq, gw, om, nm, lq_m, fm, c.c1, false);
+        redo_ambiguous<FV>(av, cv, vq, gw, ov, nv, lq_v, fv, c.c2, true);
+    }
     if (nm.flags & kPoison) { cm[0] = cm[1] = cm[2] = cm[3] = 0x7F7F7F7Fu; }
     if (nv.flags & kPoison) { cv[0] = cv[1] = cv[2] = cv[3] = 0x7F7F7F7Fu; }
 
@@ -915,30 +980,68 @@ __device__ __forceinline__ int64_t wave_id() {
     return (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 }
 
+// Full tiles of one tensor, then its final partial tile (if any).
 template <int FM, int FV>
 __global__ __launch_bounds__(kBlock) void step_single_kernel(TensorRef t, StepConsts c) {
     __shared__ ConstTables ct;
     fill_tables<FM, FV>(ct, c.b1, c.b2);
+    const int64_t full = t.n / kTile;
     const int64_t tiles = (t.n + kTile - 1) / kTile;
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t tile = wave_id(); tile < tiles; tile += nw) step_tile<FM, FV>(t, tile, c, ct);
+    int64_t first = 0;
+    if (c.lg2_group >= 5) {
+        for (int64_t tile = wave_id(); tile < full; tile += nw) {
+            TileIn in;
+            load_full_tile(t, tile, c.lg2_group, in);
+            step_tile<FM, FV, true>(t, tile, c, ct, in);
+        }
+        first = full;
+    }
+    // general path: remaining tiles (all of them for group 16)
+    for (int64_t tile = first + wave_id(); tile < tiles; tile += nw) {
+        TileIn in;
+        load_tile(t, tile, c.lg2_group, in);
+        step_tile<FM, FV, false>(t, tile, c, ct, in);
+    }
 }
 
-// Multi-tensor: descriptors and the tile prefix (count + 1 entries) live in
-// device workspace; each wavefront strides over the global tile index space
-// and walks the prefix forward to find the tensor of its tile.
+// Multi-tensor: descriptors, the prefix of full tiles per tensor (count + 1
+// entries) and the list of tensors with a partial last tile live in device
+// workspace. Each wavefront strides over the global full-tile index space,
+// walking the prefix forward to find the tensor of its tile; then the partial
+// tiles take the general path.
 template <int FM, int FV>
 __global__ __launch_bounds__(kBlock) void step_multi_kernel(const TensorRef* __restrict__ ts,
-                                                            const int64_t* __restrict__ tile_begin,
-                                                            int count, StepConsts c) {
+                                                            const int64_t* __restrict__ full_begin,
+                                                            const int32_t* __restrict__ partial, int count,
+                                                            int n_partial, StepConsts c) {
     __shared__ ConstTables ct;
     fill_tables<FM, FV>(ct, c.b1, c.b2);
-    const int64_t tiles = tile_begin[count];
+    const int64_t full = full_begin[count];
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
-    int cur = 0;
-    for (int64_t tile = wave_id(); tile < tiles; tile += nw) {
-        while (tile >= tile_begin[cur + 1]) ++cur;
-        step_tile<FM, FV>(ts[cur], tile - tile_begin[cur], c, ct);
+    if (c.lg2_group >= 5) {
+        int cur = 0;
+        for (int64_t tile = wave_id(); tile < full; tile += nw) {
+            while (tile >= full_begin[cur + 1]) ++cur;
+            TileIn in;
+            load_full_tile(ts[cur], tile - full_begin[cur], c.lg2_group, in);
+            step_tile<FM, FV, true>(ts[cur], tile - full_begin[cur], c, ct, in);
+        }
+    } else {
+        int cur = 0;
+        for (int64_t tile = wave_id(); tile < full; tile += nw) {
+            while (tile >= full_begin[cur + 1]) ++cur;
+            TileIn in;
+            load_tile(ts[cur], tile - full_begin[cur], c.lg2_group, in);
+            step_tile<FM, FV, false>(ts[cur], tile - full_begin[cur], c, ct, in);
+        }
+    }
+    for (int64_t i = wave_id(); i < n_partial; i += nw) {
+        const TensorRef& t = ts[partial[i]];
+        const int64_t tile = t.n / kTile;
+        TileIn in;
+        load_tile(t, tile, c.lg2_group, in);
+        step_tile<FM, FV, false>(t, tile, c, ct, in);
     }
 }
 
@@ -1015,7 +1118,7 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
                 const uint32_t code = (ng.flags & kSlow)
                                           ? exact_code_full<F>(xd, ng)
                                           : ((__builtin_signbit(xd) ? 0x80u : 0u) |
-                                             exact_mag(__builtin_fabs(xd), lo, ng, ct.lqm[0], mid, fr));
+                                             exact_mag<F>(__builtin_fabs(xd), lo, ng, mid, fr));
                 const uint32_t mask = ~(0xFFu << (8 * bi)), ins = code << (8 * bi);
                 const uint32_t clear = ~(0x80u << (8 * bi));
                 if (wi == 0) { cw[0] = (cw[0] & mask) | ins; amb[0] &= clear; }
@@ -1207,10 +1310,10 @@ void launch_single(const TensorRef& t, const StepConsts& c, hipStream_t st) {
 }
 
 template <int FM, int FV>
-void launch_multi(const TensorRef* ts, const int64_t* tb, int count, int64_t tiles, const StepConsts& c,
-                  hipStream_t st) {
+void launch_multi(const TensorRef* ts, const int64_t* fb, const int32_t* partial, int count, int n_partial,
+                  int64_t tiles, const StepConsts& c, hipStream_t st) {
     hipLaunchKernelGGL((step_multi_kernel<FM, FV>), dim3(grid_for(tiles, kStepBlocksPerCU)), dim3(kBlock),
-                       0, st, ts, tb, count, c);
+                       0, st, ts, fb, partial, count, n_partial, c);
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1221,7 +1324,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 extern "C" {
 
-int coat_abi_version(void) { return 100; }
+int coat_abi_version(void) { return 101; }
 
 const char* coat_strerror(int status) {
     switch (status) {
@@ -1253,9 +1356,13 @@ int coat_fp8_adamw_step(float* params, uint16_t* params_bf16, const uint16_t* gr
     return launch_status();
 }
 
+// Workspace layout: descriptors, the full-tile prefix (count + 1 int64), the
+// indices of tensors with a partial last tile (count int32), each section
+// 256-byte aligned.
 size_t coat_multi_workspace_bytes(int32_t count) {
     if (count < 0) return 0;
-    return align_up(sizeof(TensorRef) * (size_t)count, 256) + align_up(sizeof(int64_t) * ((size_t)count + 1), 256);
+    return align_up(sizeof(TensorRef) * (size_t)count, 256) + align_up(sizeof(int64_t) * ((size_t)count + 1), 256) +
+           align_up(sizeof(int32_t) * (size_t)count, 256);
 }
 
 int coat_multi_plan_init(coat_multi_plan* plan, const coat_tensor* tensors, int32_t count, void* workspace,
@@ -1264,20 +1371,25 @@ int coat_multi_plan_init(coat_multi_plan* plan, const coat_tensor* tensors, int3
     if (!workspace || workspace_bytes < coat_multi_workspace_bytes(count)) return COAT_EINVAL;
     if (!aligned(workspace, 256)) return COAT_EALIGN;
     const size_t desc_bytes = align_up(sizeof(TensorRef) * (size_t)count, 256);
-    const size_t total = desc_bytes + sizeof(int64_t) * ((size_t)count + 1);
+    const size_t fb_bytes = align_up(sizeof(int64_t) * ((size_t)count + 1), 256);
+    const size_t total = coat_multi_workspace_bytes(count);
     std::vector<char> host(total, 0);
     TensorRef* hd = reinterpret_cast<TensorRef*>(host.data());
-    int64_t* tb = reinterpret_cast<int64_t*>(host.data() + desc_bytes);
-    int64_t tiles = 0, n_total = 0;
+    int64_t* fb = reinterpret_cast<int64_t*>(host.data() + desc_bytes);
+    int32_t* partial = reinterpret_cast<int32_t*>(host.data() + desc_bytes + fb_bytes);
+    int64_t full = 0, tiles = 0, n_total = 0;
+    int32_t n_partial = 0;
     for (int32_t i = 0; i < count; ++i) {
         memcpy(&hd[i], &tensors[i], sizeof(TensorRef));
         const int rc = check_tensor(hd[i]);
         if (rc) return rc;
-        tb[i] = tiles;
+        fb[i] = full;
+        full += hd[i].n / kTile;
+        if (hd[i].n % kTile) partial[n_partial++] = i;
         tiles += (hd[i].n + kTile - 1) / kTile;
         n_total += hd[i].n;
     }
-    tb[count] = tiles;
+    fb[count] = full;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (hipMemcpyAsync(workspace, host.data(), total, hipMemcpyHostToDevice, st) != hipSuccess) return COAT_EHIP;
     if (hipStreamSynchronize(st) != hipSuccess) return COAT_EHIP;
@@ -1285,6 +1397,7 @@ int coat_multi_plan_init(coat_multi_plan* plan, const coat_tensor* tensors, int3
     plan->count = count;
     plan->tiles = tiles;
     plan->n_total = n_total;
+    plan->n_partial = n_partial;
     return COAT_OK;
 }
 
@@ -1298,15 +1411,18 @@ int coat_fp8_adamw_step_planned(const coat_multi_plan* plan, int32_t group, int3
     if (plan->count == 0 || plan->tiles == 0) return COAT_OK;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const size_t desc_bytes = align_up(sizeof(TensorRef) * (size_t)plan->count, 256);
-    const TensorRef* dts = static_cast<const TensorRef*>(plan->workspace);
-    const int64_t* dtb = reinterpret_cast<const int64_t*>(static_cast<const char*>(plan->workspace) + desc_bytes);
+    const size_t fb_bytes = align_up(sizeof(int64_t) * ((size_t)plan->count + 1), 256);
+    const char* ws = static_cast<const char*>(plan->workspace);
+    const TensorRef* dts = reinterpret_cast<const TensorRef*>(ws);
+    const int64_t* dfb = reinterpret_cast<const int64_t*>(ws + desc_bytes);
+    const int32_t* dpt = reinterpret_cast<const int32_t*>(ws + desc_bytes + fb_bytes);
     const int fm = fmt_m & 0xFF, fv = fmt_v & 0xFF;
-    const int count = plan->count;
+    const int count = plan->count, np = plan->n_partial;
     const int64_t tiles = plan->tiles;
-    if (fm == COAT_FMT_E4M3 && fv == COAT_FMT_E4M3) launch_multi<COAT_FMT_E4M3, COAT_FMT_E4M3>(dts, dtb, count, tiles, c, st);
-    else if (fm == COAT_FMT_E4M3) launch_multi<COAT_FMT_E4M3, COAT_FMT_E5M2>(dts, dtb, count, tiles, c, st);
-    else if (fv == COAT_FMT_E4M3) launch_multi<COAT_FMT_E5M2, COAT_FMT_E4M3>(dts, dtb, count, tiles, c, st);
-    else launch_multi<COAT_FMT_E5M2, COAT_FMT_E5M2>(dts, dtb, count, tiles, c, st);
+    if (fm == COAT_FMT_E4M3 && fv == COAT_FMT_E4M3) launch_multi<COAT_FMT_E4M3, COAT_FMT_E4M3>(dts, dfb, dpt, count, np, tiles, c, st);
+    else if (fm == COAT_FMT_E4M3) launch_multi<COAT_FMT_E4M3, COAT_FMT_E5M2>(dts, dfb, dpt, count, np, tiles, c, st);
+    else if (fv == COAT_FMT_E4M3) launch_multi<COAT_FMT_E5M2, COAT_FMT_E4M3>(dts, dfb, dpt, count, np, tiles, c, st);
+    else launch_multi<COAT_FMT_E5M2, COAT_FMT_E5M2>(dts, dfb, dpt, count, np, tiles, c, st);
     return launch_status();
 }
 

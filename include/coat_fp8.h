@@ -112,10 +112,11 @@ size_t coat_multi_workspace_bytes(int32_t count);
  * table and the tile table live in caller-owned device workspace.
  */
 typedef struct coat_multi_plan {
-    void* workspace;  /* device memory holding the tables */
-    int32_t count;    /* tensors */
-    int64_t tiles;    /* 1024-element tiles across all tensors */
-    int64_t n_total;  /* parameters across all tensors */
+    void* workspace;    /* device memory holding the tables */
+    int32_t count;      /* tensors */
+    int64_t tiles;      /* 1024-element tiles across all tensors */
+    int64_t n_total;    /* parameters across all tensors */
+    int32_t n_partial;  /* tensors whose size is not a multiple of 1024 */
 } coat_multi_plan;
 
 /*

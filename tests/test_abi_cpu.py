@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_static_helpers():
     L = coat.lib()
-    assert L.coat_abi_version() == 100
+    assert L.coat_abi_version() == 101
     assert coat.strerror(0) == "ok" and "invalid" in coat.strerror(-1)
     assert L.coat_multi_workspace_bytes(363) >= 363 * 80 + 364 * 8
     assert L.coat_multi_workspace_bytes(363) % 256 == 0
