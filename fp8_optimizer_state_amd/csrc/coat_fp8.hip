@@ -118,14 +118,14 @@ __device__ __forceinline__ FmtRT fmt_rt() {
 // ------------------------------------------------------------------ fp64 math
 //
 // exp2: u = n + f with n = rint(u), |f| <= 1/2, and 2^f = exp(f ln 2). The
-// per-group routine uses its Taylor series sum (ln 2)^i f^i / i! to degree 13
-// (truncation below 2^-57 on |f| <= 1/2). The per-element routine uses the
-// degree-10 polynomial interpolating 2^f at the eleven Chebyshev nodes of
-// [-1/2, 1/2] (relative error below 2^-51.5). The smallest member of a group
-// is usually a near-cancellation b1*m + (1-b1)*g whose relative error is the
-// dequantization error amplified by |b1*m| / |m'| (1e8 and more in the tails
-// of a 13e9-element step), and k and s follow it, so the dequantized moments
-// are kept within a few 1e-15.
+// polynomial is the degree-10 one interpolating 2^f at the eleven Chebyshev
+// nodes of [-1/2, 1/2] (relative error below 2^-51.5), shared by every use so
+// that the kernels hold only one set of its constants (fp64 operands cannot be
+// instruction literals here; they occupy registers). The smallest member of a
+// group is usually a near-cancellation b1*m + (1-b1)*g whose relative error is
+// the dequantization error amplified by |b1*m| / |m'| (1e8 and more in the
+// tails of a 13e9-element step), and k and s follow it, so the dequantized
+// moments are kept within a few 1e-15.
 // log2: x = m 2^e with m in [sqrt(1/2), sqrt(2)), u = (m-1)/(m+1), and
 // ln m = 2 atanh(u) = 2 sum u^(2j+1) / (2j+1); |u| <= 0.1716, so 12 terms
 // reach 2^-56. Quotients and reciprocals use the hardware reciprocal estimate
@@ -147,23 +147,6 @@ __device__ __forceinline__ double exp2_poly10(double f) {
     return p;
 }
 
-__device__ __forceinline__ double exp2_poly13(double f) {
-    double p = 0x1.816193166d0f9p-40;
-    p = __builtin_fma(p, f, 0x1.c3bd650fc2986p-36);
-    p = __builtin_fma(p, f, 0x1.e8cac7351bb25p-32);
-    p = __builtin_fma(p, f, 0x1.e4cf5158b8ecap-28);
-    p = __builtin_fma(p, f, 0x1.b5253d395e7c4p-24);
-    p = __builtin_fma(p, f, 0x1.62c0223a5c824p-20);
-    p = __builtin_fma(p, f, 0x1.ffcbfc588b0c7p-17);
-    p = __builtin_fma(p, f, 0x1.430912f86c787p-13);
-    p = __builtin_fma(p, f, 0x1.5d87fe78a6731p-10);
-    p = __builtin_fma(p, f, 0x1.3b2ab6fba4e77p-7);
-    p = __builtin_fma(p, f, 0x1.c6b08d704a0c0p-5);
-    p = __builtin_fma(p, f, 0x1.ebfbdff82c58fp-3);
-    p = __builtin_fma(p, f, 0x1.62e42fefa39efp-1);
-    p = __builtin_fma(p, f, 1.0);
-    return p;
-}
 
 // v_cvt_i32_f64 clamps out-of-range values to INT_MIN / INT_MAX and maps NaN
 // to 0; spelled out so that the compiler cannot treat overflow as undefined.
@@ -201,7 +184,7 @@ __device__ __forceinline__ double vmin_abs(double a, double b) {
 __device__ __forceinline__ double exp2_full(double u) {
     double n = __builtin_rint(u);
     double f = u - n;
-    return __builtin_amdgcn_ldexp(exp2_poly13(f), cvt_i32_sat(n));
+    return __builtin_amdgcn_ldexp(exp2_poly10(f), cvt_i32_sat(n));
 }
 
 // 1/b for finite normal b: hardware estimate plus two Newton steps.
@@ -366,13 +349,16 @@ __device__ float decode_value(uint32_t code) {
 //            maps to -1e300 and Inf to +1e300 so that the same arithmetic yields
 //            0 and Inf, NaN codes to NaN), and b = the moment's decay with the
 //            code's sign (the step's first operation on the dequantized value
-//            is b x; the codec kernels use b = 1).
+//            is b x; the codec kernels use b = 1);
+//   lqm[c] = log2(midpoint(c, c+1) / fpmax), the per-code constant of the
+//            exact requantization threshold.
 struct alignas(16) LqEntry {
     double lq;
     double b;
 };
 struct ConstTables {
     LqEntry lqb[2][256];
+    double lqm[2][128];
 };
 
 template <int F>
@@ -393,8 +379,6 @@ __device__ double lq_entry(int c) {
     return (ip - T::LOG2_FPMAX) + fl;
 }
 
-// log2(midpoint(c, c+1) / fpmax): the constant of the exact requantization
-// threshold between magnitude codes c and c + 1 (rare path, computed on use).
 template <int F>
 __device__ double lqm_entry(int c) {
     using T = Fmt<F>;
@@ -413,6 +397,7 @@ __device__ __forceinline__ void fill_tables(ConstTables& ct, double bm, double b
     const double b = f ? bv : bm;
     ct.lqb[f][c] = LqEntry{lq, b};
     ct.lqb[f][c | 128] = LqEntry{lq, -b};
+    ct.lqm[f][c] = f ? lqm_entry<FV>(c) : lqm_entry<FM>(c);
     __syncthreads();
 }
 
@@ -529,9 +514,8 @@ __device__ __forceinline__ NewGroup swap_pair(const NewGroup& g) {
 // y = fpmax (|x| / amax)^k against that midpoint, ties to the even code. For
 // k = 1 the expanded value is formed as fpmax (|x| / amax) with IEEE
 // operations; otherwise |x| is compared with amax 2^(log2(mid / fpmax) / k).
-template <int FMT>
-__device__ __forceinline__ uint32_t exact_mag(double ax, uint32_t lo, const NewGroup& g, double mid,
-                                              const FmtRT& F) {
+__device__ __forceinline__ uint32_t exact_mag(double ax, uint32_t lo, const NewGroup& g, const double* lqm,
+                                              double mid, const FmtRT& F) {
     bool up;
     bool tie;
     if (g.k == 1.0f) {
@@ -539,7 +523,7 @@ __device__ __forceinline__ uint32_t exact_mag(double ax, uint32_t lo, const NewG
         up = y > mid;
         tie = y == mid;
     } else {
-        const double thr = g.amax * exp2_full(lqm_entry<FMT>((int)lo) * g.r);
+        const double thr = g.amax * exp2_full(lqm[lo] * g.r);
         up = ax > thr;
         tie = ax == thr;
     }
@@ -638,24 +622,38 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t word, int half) {
     return (double)__builtin_bit_cast(float, half ? (word & 0xFFFF0000u) : (word << 16));
 }
 
+// Per-wave LDS area holding, after the element pass, the inputs that only the
+// exact requantization needs (raw codes and grads, dequantization constants),
+// so that no registers are held for them through the requantization.
+struct Park {
+    uint32_t gw[8][kWave];
+    uint32_t mq[4][kWave];
+    uint32_t vq[4][kWave];
+    double og[6][kWave];  // m: a, a_lo, r; v: a, a_lo, r
+};
+
 // Exact decision for the elements whose fast code is flagged in `amb` (one
 // moment): the element's new moment is recomputed in fp64 exactly as in the
-// main pass, then rounded with the fp64 threshold (or from scratch for groups
-// outside the fp32 path's range). Loops until no lane has a flagged element.
+// main pass (its old code, grad and the dequantization constants read back
+// from the park area; `old` is the moment's code rows, og_row its first
+// constant row), then rounded with the fp64 threshold (or from scratch for
+// groups outside the fp32 path's range). Loops until no lane has a flagged
+// element.
 template <int F>
-__device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&codes)[4], const uint32_t (&old)[4],
-                                               const uint32_t (&gw)[8], const OldGroup& og, const NewGroup& ng,
-                                               const LqEntry* lq, const FmtRT& F_,
-                                               double cb, bool square) {
+__device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&codes)[4],
+                                               const uint32_t (*old)[kWave], const Park& pk, int og_row,
+                                               const NewGroup& ng, const LqEntry* lq, const double* lqm,
+                                               const FmtRT& F_, double cb, bool square) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const OldGroup og{pk.og[og_row][lane], pk.og[og_row + 1][lane], pk.og[og_row + 2][lane]};
     while (__any((amb[0] | amb[1] | amb[2] | amb[3]) != 0u)) {
         if ((amb[0] | amb[1] | amb[2] | amb[3]) != 0u) {
             const int wi = amb[0] ? 0 : (amb[1] ? 1 : (amb[2] ? 2 : 3));
             const uint32_t aw = select4(wi, amb[0], amb[1], amb[2], amb[3]);
             const int bi = __builtin_ctz(aw) >> 3;
             const int e = 4 * wi + bi;
-            const uint32_t oldw = select4(wi, old[0], old[1], old[2], old[3]);
-            const uint32_t gword = (e >> 1) < 4 ? select4(e >> 1, gw[0], gw[1], gw[2], gw[3])
-                                                : select4((e >> 1) - 4, gw[4], gw[5], gw[6], gw[7]);
+            const uint32_t oldw = old[wi][lane];
+            const uint32_t gword = pk.gw[e >> 1][lane];
             const double g = bf16_to_f64(gword, e & 1);
             double tb;
             const double mag = dequant_mag(oldw >> (8 * bi), 0, og, lq, tb);
@@ -667,7 +665,7 @@ __device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&co
                 code = exact_code_full<F>(x, ng);
             } else {
                 const double mid = 0.5 * (value_of<F>(lo) + value_of<F>(lo + 1));
-                code = (__builtin_signbit(x) ? 0x80u : 0u) | exact_mag<F>(__builtin_fabs(x), lo, ng, mid, F_);
+                code = (__builtin_signbit(x) ? 0x80u : 0u) | exact_mag(__builtin_fabs(x), lo, ng, lqm, mid, F_);
             }
             const uint32_t mask = ~(0xFFu << (8 * bi)), ins = code << (8 * bi);
             const uint32_t clear = ~(0x80u << (8 * bi));
@@ -786,7 +784,7 @@ __device__ __forceinline__ void load_full_tile(const TensorRef& t, int64_t tile,
 // split over lane pairs (group >= 32), so no lane needs a bounds check.
 template <int FM, int FV, bool FULL>
 __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
-                                          const ConstTables& ct, TileIn& in) {
+                                          const ConstTables& ct, Park& pk, TileIn& in) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
     const int64_t rem = t.n - e0;
@@ -850,20 +848,30 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     // A zero moment (the minimum is over nonzero members) or a non-finite one:
     // the statistics are redone exactly.
     const bool special = amin_m == 0.0 || amin_v == 0.0 || !(__builtin_fabsf(fin) <= 0x1.fffffep+127f);
+    // ---- park what only the exact paths (statistics with zeros, requantization) need
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pk.gw[i][lane] = gw[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { pk.mq[i][lane] = mq[i]; pk.vq[i][lane] = vq[i]; }
+    pk.og[0][lane] = om.a; pk.og[1][lane] = om.a_lo; pk.og[2][lane] = om.r;
+    pk.og[3][lane] = ov.a; pk.og[4][lane] = ov.a_lo; pk.og[5][lane] = ov.r;
+    // later reads of the park area must come from LDS, not from registers
+    asm volatile("" ::: "memory");
+
     bool bad = false;
     if (__any(special)) {
         // Rare: exact statistics with zeros excluded from the minimum and
-        // non-finite moments flagged.
+        // non-finite moments flagged, from the parked inputs.
+        const OldGroup pm{pk.og[0][lane], pk.og[1][lane], pk.og[2][lane]};
+        const OldGroup pv{pk.og[3][lane], pk.og[4][lane], pk.og[5][lane]};
         amax_m = 0.0; amin_m = __builtin_inf(); amax_v = 0.0; amin_v = __builtin_inf();
         for (int i = 0; i < 16; ++i) {
-            const uint32_t wm = select4(i >> 2, mq[0], mq[1], mq[2], mq[3]);
-            const uint32_t wv = select4(i >> 2, vq[0], vq[1], vq[2], vq[3]);
-            const uint32_t gword = (i >> 1) < 4 ? select4(i >> 1, gw[0], gw[1], gw[2], gw[3])
-                                                : select4((i >> 1) - 4, gw[4], gw[5], gw[6], gw[7]);
-            const double g = bf16_to_f64(gword, i & 1);
+            const uint32_t wm = pk.mq[i >> 2][lane];
+            const uint32_t wv = pk.vq[i >> 2][lane];
+            const double g = bf16_to_f64(pk.gw[i >> 1][lane], i & 1);
             double tbm, tbv;
-            const double m0 = dequant_mag(wm >> (8 * (i & 3)), 0, om, lq_m, tbm);
-            const double v0 = dequant_mag(wv >> (8 * (i & 3)), 0, ov, lq_v, tbv);
+            const double m0 = dequant_mag(wm >> (8 * (i & 3)), 0, pm, lq_m, tbm);
+            const double v0 = dequant_mag(wv >> (8 * (i & 3)), 0, pv, lq_v, tbv);
             const double m1 = __builtin_fma(tbm, m0, c.c1 * g);
             const double v1 = __builtin_fma(tbv, v0, c.c2 * (g * g));
             const double am = __builtin_fabs(m1), av = __builtin_fabs(v1);
@@ -955,8 +963,8 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     if (nm.flags & kPoison) { am[0] = am[1] = am[2] = am[3] = 0u; }
     if (nv.flags & kPoison) { av[0] = av[1] = av[2] = av[3] = 0u; }
     if (__any((am[0] | am[1] | am[2] | am[3] | av[0] | av[1] | av[2] | av[3]) != 0u)) {
-        redo_ambiguous<FM>(am, cm, mq, gw, om, nm, lq_m, fm, c.c1, false);
-        redo_ambiguous<FV>(av, cv, vq, gw, ov, nv, lq_v, fv, c.c2, true);
+        redo_ambiguous<FM>(am, cm, pk.mq, pk, 0, nm, lq_m, ct.lqm[0], fm, c.c1, false);
+        redo_ambiguous<FV>(av, cv, pk.vq, pk, 3, nv, lq_v, ct.lqm[1], fv, c.c2, true);
     }
     if (nm.flags & kPoison) { cm[0] = cm[1] = cm[2] = cm[3] = 0x7F7F7F7Fu; }
     if (nv.flags & kPoison) { cv[0] = cv[1] = cv[2] = cv[3] = 0x7F7F7F7Fu; }
@@ -982,8 +990,10 @@ __device__ __forceinline__ int64_t wave_id() {
 
 // Full tiles of one tensor, then its final partial tile (if any).
 template <int FM, int FV>
-__global__ __launch_bounds__(kBlock) void step_single_kernel(TensorRef t, StepConsts c) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) void step_single_kernel(TensorRef t, StepConsts c) {
     __shared__ ConstTables ct;
+    __shared__ Park parks[kWavesPerBlock];
+    Park& pk = parks[threadIdx.x / kWave];
     fill_tables<FM, FV>(ct, c.b1, c.b2);
     const int64_t full = t.n / kTile;
     const int64_t tiles = (t.n + kTile - 1) / kTile;
@@ -993,7 +1003,7 @@ __global__ __launch_bounds__(kBlock) void step_single_kernel(TensorRef t, StepCo
         for (int64_t tile = wave_id(); tile < full; tile += nw) {
             TileIn in;
             load_full_tile(t, tile, c.lg2_group, in);
-            step_tile<FM, FV, true>(t, tile, c, ct, in);
+            step_tile<FM, FV, true>(t, tile, c, ct, pk, in);
         }
         first = full;
     }
@@ -1001,7 +1011,7 @@ __global__ __launch_bounds__(kBlock) void step_single_kernel(TensorRef t, StepCo
     for (int64_t tile = first + wave_id(); tile < tiles; tile += nw) {
         TileIn in;
         load_tile(t, tile, c.lg2_group, in);
-        step_tile<FM, FV, false>(t, tile, c, ct, in);
+        step_tile<FM, FV, false>(t, tile, c, ct, pk, in);
     }
 }
 
@@ -1011,11 +1021,13 @@ __global__ __launch_bounds__(kBlock) void step_single_kernel(TensorRef t, StepCo
 // walking the prefix forward to find the tensor of its tile; then the partial
 // tiles take the general path.
 template <int FM, int FV>
-__global__ __launch_bounds__(kBlock) void step_multi_kernel(const TensorRef* __restrict__ ts,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) void step_multi_kernel(const TensorRef* __restrict__ ts,
                                                             const int64_t* __restrict__ full_begin,
                                                             const int32_t* __restrict__ partial, int count,
                                                             int n_partial, StepConsts c) {
     __shared__ ConstTables ct;
+    __shared__ Park parks[kWavesPerBlock];
+    Park& pk = parks[threadIdx.x / kWave];
     fill_tables<FM, FV>(ct, c.b1, c.b2);
     const int64_t full = full_begin[count];
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
@@ -1025,7 +1037,7 @@ __global__ __launch_bounds__(kBlock) void step_multi_kernel(const TensorRef* __r
             while (tile >= full_begin[cur + 1]) ++cur;
             TileIn in;
             load_full_tile(ts[cur], tile - full_begin[cur], c.lg2_group, in);
-            step_tile<FM, FV, true>(ts[cur], tile - full_begin[cur], c, ct, in);
+            step_tile<FM, FV, true>(ts[cur], tile - full_begin[cur], c, ct, pk, in);
         }
     } else {
         int cur = 0;
@@ -1033,7 +1045,7 @@ __global__ __launch_bounds__(kBlock) void step_multi_kernel(const TensorRef* __r
             while (tile >= full_begin[cur + 1]) ++cur;
             TileIn in;
             load_tile(ts[cur], tile - full_begin[cur], c.lg2_group, in);
-            step_tile<FM, FV, false>(ts[cur], tile - full_begin[cur], c, ct, in);
+            step_tile<FM, FV, false>(ts[cur], tile - full_begin[cur], c, ct, pk, in);
         }
     }
     for (int64_t i = wave_id(); i < n_partial; i += nw) {
@@ -1041,7 +1053,7 @@ __global__ __launch_bounds__(kBlock) void step_multi_kernel(const TensorRef* __r
         const int64_t tile = t.n / kTile;
         TileIn in;
         load_tile(t, tile, c.lg2_group, in);
-        step_tile<FM, FV, false>(t, tile, c, ct, in);
+        step_tile<FM, FV, false>(t, tile, c, ct, pk, in);
     }
 }
 
@@ -1118,7 +1130,7 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
                 const uint32_t code = (ng.flags & kSlow)
                                           ? exact_code_full<F>(xd, ng)
                                           : ((__builtin_signbit(xd) ? 0x80u : 0u) |
-                                             exact_mag<F>(__builtin_fabs(xd), lo, ng, mid, fr));
+                                             exact_mag(__builtin_fabs(xd), lo, ng, ct.lqm[0], mid, fr));
                 const uint32_t mask = ~(0xFFu << (8 * bi)), ins = code << (8 * bi);
                 const uint32_t clear = ~(0x80u << (8 * bi));
                 if (wi == 0) { cw[0] = (cw[0] & mask) | ins; amb[0] &= clear; }
