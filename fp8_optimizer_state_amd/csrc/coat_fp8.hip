@@ -56,11 +56,20 @@ constexpr int kBlock = 256;                // 4 wavefronts
 constexpr int kWavesPerBlock = kBlock / kWave;
 
 // Relative half-width of the window around an FP8 rounding midpoint inside
-// which the fp32 fast path defers to the exact fp64 decision. The fast path's
-// error stays below about 7e-6 relative (native log2/exp2 of arguments up to
-// 32 in magnitude and three fp32 roundings of |x| / amax amplified by k);
-// 2^-15 = 3.05e-5 keeps a margin of more than 4x.
+// which a converted value is decided exactly (plain encoding, no transcendentals).
 constexpr float kAmbiguity = 0x1p-15f;
+
+// Window of the requantization fast path, per group: w = W0 + W1 k relative.
+// The fast path forms y = 2^(k log2(|x| / amax) + log2 fpmax) in fp32. Its
+// error: |x| / amax carries three fp32 roundings (<= 3 * 2^-24 relative, k
+// times that in y); v_log_f32 is accurate to about an ulp of its result, whose
+// magnitude times k stays below log2 R_fp8 (17.8 for E4M3, 31.8 for E5M2), so
+// k times that error stays below log2(R_fp8) * 2^-23; the fma adds half an
+// ulp of |z| <= 16; v_exp_f32 about an ulp. In total below ln 2 * (2^-23
+// log2 R_fp8 + 2^-20 + k * 2.6e-7) + 1.2e-7, i.e. 2.2e-6 + 1.8e-7 k (E4M3)
+// and 3.4e-6 + 1.8e-7 k (E5M2); measured maxima on gfx950 over 1.6e7 samples
+// per k sit at 55-70 % of that. W0 and W1 take twice the bound.
+constexpr float kAmbW1 = 3.6e-7f;
 
 template <typename T>
 __device__ __forceinline__ __attribute__((address_space(1))) T* gp(T* p) {
@@ -83,6 +92,7 @@ struct Fmt<COAT_FMT_E4M3> {
     static constexpr double LOG2_FPMAX = 0x1.19d5d9fd5010bp+3;  // log2(448)
     static constexpr double LOG2_FPMAX_LO = 0x1.b332ac903a414p-52;  // its rounding error
     static constexpr float LOG2_FPMAX_F = 0x1.19d5dap+3f;
+    static constexpr float AMB_W0 = 4.4e-6f;  // fast-path window, see kAmbW1
     static constexpr double LOG2_RF = 0x1.1ceaecfea8086p+4;     // log2(448 / 2^-9)
     __device__ static bool is_nan(int c) { return c == 0x7F; }
     __device__ static bool is_inf(int) { return false; }
@@ -99,6 +109,7 @@ struct Fmt<COAT_FMT_E5M2> {
     static constexpr double LOG2_FPMAX = 0x1.f9d5d9fd5010bp+3;  // log2(57344)
     static constexpr double LOG2_FPMAX_LO = 0x1.b332ac903a414p-52;  // its rounding error
     static constexpr float LOG2_FPMAX_F = 0x1.f9d5dap+3f;
+    static constexpr float AMB_W0 = 6.8e-6f;  // fast-path window, see kAmbW1
     static constexpr double LOG2_RF = 0x1.fceaecfea8086p+4;     // log2(57344 / 2^-16)
     __device__ static bool is_nan(int c) { return c > 0x7C; }
     __device__ static bool is_inf(int c) { return c == 0x7C; }
@@ -107,12 +118,12 @@ struct Fmt<COAT_FMT_E5M2> {
 // Per-lane format constants, for code that serves both moments at once.
 struct FmtRT {
     double fpmax, log2_fpmax, log2_fpmax_lo, log2_rf;
-    float fpmax_f, log2_fpmax_f;
+    float fpmax_f, log2_fpmax_f, amb_w0;
 };
 template <int F>
 __device__ __forceinline__ FmtRT fmt_rt() {
     using T = Fmt<F>;
-    return FmtRT{T::FPMAX, T::LOG2_FPMAX, T::LOG2_FPMAX_LO, T::LOG2_RF, T::FPMAX_F, T::LOG2_FPMAX_F};
+    return FmtRT{T::FPMAX, T::LOG2_FPMAX, T::LOG2_FPMAX_LO, T::LOG2_RF, T::FPMAX_F, T::LOG2_FPMAX_F, T::AMB_W0};
 }
 
 // ------------------------------------------------------------------ fp64 math
@@ -443,6 +454,7 @@ struct NewGroup {
     double r;      // 1 / k in fp64 (exact path)
     float k;       // stored exponent
     float ia;      // 1 / amax in fp32 (0 for an all-zero group)
+    float w;       // the fast path's ambiguity window for this k
     uint32_t flags;
 };
 constexpr uint32_t kPoison = 1u;  // non-finite member: every code 0x7F
@@ -456,6 +468,7 @@ __device__ NewGroup new_group(double amax, double amin, bool poison, bool expand
     g.amax = amax;
     g.flags = 0;
     g.r = 1.0;
+    g.w = 0.0f;
     if (poison) {
         g.s = __builtin_nan("");
         g.k = 1.0f;
@@ -488,6 +501,7 @@ __device__ NewGroup new_group(double amax, double amin, bool poison, bool expand
     g.r = rcp_f64((double)k);
     g.s = exp2_full((double)k * L - F.log2_fpmax);
     g.ia = (float)rcp_f64(amax);
+    g.w = __builtin_fmaf(kAmbW1, k, F.amb_w0);
     // The fp32 path needs every member and 1/amax normal in fp32 and |x| / amax
     // at least 2^-100 for nonzero members.
     if (!(amax <= 0x1p126 && amin >= 0x1p-126 && R <= 0x1p100)) g.flags = kSlow;
@@ -505,6 +519,7 @@ __device__ __forceinline__ NewGroup swap_pair(const NewGroup& g) {
     o.r = dpp64<kDppXor1>(g.r);
     o.k = __builtin_bit_cast(float, dpp32<kDppXor1>(__builtin_bit_cast(uint32_t, g.k)));
     o.ia = __builtin_bit_cast(float, dpp32<kDppXor1>(__builtin_bit_cast(uint32_t, g.ia)));
+    o.w = __builtin_bit_cast(float, dpp32<kDppXor1>(__builtin_bit_cast(uint32_t, g.w)));
     o.flags = dpp32<kDppXor1>(g.flags);
     return o;
 }
@@ -559,9 +574,9 @@ __device__ __forceinline__ uint32_t fast_codes4(const float* xf, const NewGroup&
         const float l = __builtin_amdgcn_logf(t);
         const float z = __builtin_fmaf(g.k, l, T::LOG2_FPMAX_F);
         const float y = __builtin_amdgcn_exp2f(z);
-        lo[i] = __builtin_copysignf(y * (1.0f - kAmbiguity), xf[i]);
+        lo[i] = __builtin_copysignf(__builtin_fmaf(-y, g.w, y), xf[i]);
         // y <= fpmax (1 + 1e-5) here, far below the overflow midpoint, so no clamp
-        hi[i] = y * (1.0f + kAmbiguity);
+        hi[i] = __builtin_fmaf(y, g.w, y);
     }
     // The second convert writes the high halves, so the first one's
     // passthrough operand may be any register that dies there.
@@ -795,7 +810,12 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     // stored even by lanes past the end, which take part in the pair's work.
     const bool gvalid = FULL || (gidx << c.lg2_group) < t.n;
     const bool pair = FULL || lpg >= 2;      // per-group work split over a lane pair
-    const bool odd = (lane & 1) != 0;
+    // Opaque to the optimizer, so that the per-lane choices between the two
+    // formats' constants are made in each tile rather than held in registers
+    // (spilled) across the tile loop.
+    int odd_bit = lane & 1;
+    asm volatile("" : "+v"(odd_bit));
+    const bool odd = odd_bit != 0;
     const FmtRT fm = fmt_rt<FM>(), fv = fmt_rt<FV>();
 
     gfloat* P = gp(t.p);
