@@ -463,7 +463,17 @@ constexpr uint32_t kSlow = 2u;    // fp32 fast path unsafe for this group: exact
 // k = ln R_fp8 / ln(amax / amin) (= log2 R_fp8 / log2 R), k = 1 for an
 // all-zero or near-constant group or without expansion; then the range guard:
 // amax^k and amax^k / R_fp8 within [2^-1022, 2^1023]; s = amax^k / fpmax.
-__device__ NewGroup new_group(double amax, double amin, bool poison, bool expand, const FmtRT& F) {
+// log2 of x (hi + lo) for finite x > 0; 0 for anything else (values a caller
+// does not use: zero or infinite statistics of empty or poisoned groups).
+__device__ __forceinline__ double log2_stat(double x, double& lo) {
+    const double xs = (x > 0.0 && x < __builtin_inf()) ? x : 1.0;
+    return log2_full_dd(xs, lo);
+}
+
+// L + L_lo = log2(amax), Lm + Lm_lo = log2(amin) (as from log2_stat); the
+// group's log2(amax / amin) is their double-double difference.
+__device__ NewGroup new_group(double amax, double amin, double L, double L_lo, double Lm, double Lm_lo,
+                              bool poison, bool expand, const FmtRT& F) {
     NewGroup g;
     g.amax = amax;
     g.flags = 0;
@@ -482,10 +492,10 @@ __device__ NewGroup new_group(double amax, double amin, bool poison, bool expand
         g.ia = 0.0f;
         return g;
     }
-    const double L = log2_full(amax);
     float k = 1.0f;
-    const double R = div_f64(amax, amin);
-    if (expand && R > 1.000001) k = (float)(F.log2_rf * rcp_f64(log2_full(R)));
+    const double d = L - Lm;
+    const double log2R = d + (((L - d) - Lm) + (L_lo - Lm_lo));
+    if (expand && amax > amin * 1.000001) k = (float)(F.log2_rf * rcp_f64(log2R));
     const double lo = -1022.0 + F.log2_rf, hi = 1023.0;
     const double kL = (double)k * L;
     if (!(kL >= lo && kL <= hi)) {
@@ -504,7 +514,7 @@ __device__ NewGroup new_group(double amax, double amin, bool poison, bool expand
     g.w = __builtin_fmaf(kAmbW1, k, F.amb_w0);
     // The fp32 path needs every member and 1/amax normal in fp32 and |x| / amax
     // at least 2^-100 for nonzero members.
-    if (!(amax <= 0x1p126 && amin >= 0x1p-126 && R <= 0x1p100)) g.flags = kSlow;
+    if (!(amax <= 0x1p126 && amin >= 0x1p-126 && log2R <= 100.0)) g.flags = kSlow;
     return g;
 }
 
@@ -941,7 +951,24 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     // ---- requantization constants (the lane pair splits the two moments)
     NewGroup nm, nv;
     if (pair) {
-        const NewGroup mine = new_group(odd ? amax_v : amax_m, odd ? amin_v : amin_m, poison,
+        const double amax_x = odd ? amax_v : amax_m, amin_x = odd ? amin_v : amin_m;
+        double L, L_lo, Lm, Lm_lo;
+        if (lpg >= 4) {
+            // lane quad: lanes 0, 1 take log2 of the m and v maxima, lanes 2, 3
+            // of the minima, and partners (lane ^ 2) swap them
+            const bool hiq = (lane & 2) != 0;
+            double xl_lo;
+            const double xl = log2_stat(hiq ? amin_x : amax_x, xl_lo);
+            const double yl = dpp64<kDppXor2>(xl), yl_lo = dpp64<kDppXor2>(xl_lo);
+            L = hiq ? yl : xl;
+            L_lo = hiq ? yl_lo : xl_lo;
+            Lm = hiq ? xl : yl;
+            Lm_lo = hiq ? xl_lo : yl_lo;
+        } else {
+            L = log2_stat(amax_x, L_lo);
+            Lm = log2_stat(amin_x, Lm_lo);
+        }
+        const NewGroup mine = new_group(amax_x, amin_x, L, L_lo, Lm, Lm_lo, poison,
                                         odd ? c.expand_v : c.expand_m, odd ? fv : fm);
         const NewGroup other = swap_pair(mine);
         nm = odd ? other : mine;
@@ -953,8 +980,11 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
             gp(kp)[gidx] = mine.k;
         }
     } else {
-        nm = new_group(amax_m, amin_m, poison, c.expand_m, fm);
-        nv = new_group(amax_v, amin_v, poison, c.expand_v, fv);
+        double a_lo, b_lo, c_lo, d_lo;
+        const double la = log2_stat(amax_m, a_lo), lb = log2_stat(amin_m, b_lo);
+        const double lc = log2_stat(amax_v, c_lo), ld = log2_stat(amin_v, d_lo);
+        nm = new_group(amax_m, amin_m, la, a_lo, lb, b_lo, poison, c.expand_m, fm);
+        nv = new_group(amax_v, amin_v, lc, c_lo, ld, d_lo, poison, c.expand_v, fv);
         if (nvalid > 0) {
             gp(t.ms)[gidx] = nm.s; gp(t.mk)[gidx] = nm.k;
             gp(t.vs)[gidx] = nv.s; gp(t.vk)[gidx] = nv.k;
@@ -1120,7 +1150,9 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
         amax = group_max(amax, lpg);
         amin = group_min(amin, lpg);
         const bool poison = group_or(bad ? 1u : 0u, lpg) != 0u;
-        const NewGroup ng = new_group(amax, amin, poison, expand, fr);
+        double la_lo, lb_lo;
+        const double la = log2_stat(amax, la_lo), lb = log2_stat(amin, lb_lo);
+        const NewGroup ng = new_group(amax, amin, la, la_lo, lb, lb_lo, poison, expand, fr);
         uint32_t cw[4], amb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) cw[i] = fast_codes4<F>(xf + 4 * i, ng, amb[i]);
