@@ -143,18 +143,39 @@ __device__ __forceinline__ FmtRT fmt_rt() {
 // refined by Newton steps. Coefficients are (ln 2)^i / i! and
 // 2 log2(e) / (2j+1) rounded to fp64.
 
+// Coefficients, highest degree first: 2^f on [-1/2, 1/2] (degree 10) and
+// 2 log2(e) / (2j+1) for the atanh series of log2 (in w = u^2, 12 terms).
+constexpr int kExp2N = 11;
+constexpr int kLog2N = 12;
+__device__ constexpr double kExp2C[kExp2N] = {
+    0x1.e6063f7217bc6p-28, 0x1.b675bca4eeebbp-24, 0x1.62bfd47773353p-20, 0x1.ffcb54062e698p-17,
+    0x1.430913096fd9fp-13, 0x1.5d87fe9d7a584p-10, 0x1.3b2ab6fba1ddap-7,  0x1.c6b08d703ce49p-5,
+    0x1.ebfbdff82c598p-3,  0x1.62e42fefa3a19p-1,  1.0};
+__device__ constexpr double kLog2C[kLog2N] = {
+    0x1.00ecd7e080215p-3, 0x1.1964ec6fc9491p-3, 0x1.3703c1f4d0ffep-3, 0x1.5b9ac9b743f0dp-3,
+    0x1.89f3b1694cffep-3, 0x1.c68f568d31760p-3, 0x1.0c9a84994022dp-2, 0x1.484b13d7c02a9p-2,
+    0x1.a61762a7aded9p-2, 0x1.2776c50ef9bfep-1, 0x1.ec709dc3a03fdp-1, 0x1.71547652b82fep+1};
+
+// The rare exact paths read the coefficients from an LDS copy (CoefPtr) rather
+// than holding them in registers: fp64 constants cannot be instruction literals
+// on gfx950, and register copies of them for code that seldom runs would crowd
+// out a third wave per SIMD. The per-element and per-group code on the common
+// path uses the constants directly.
+typedef const __attribute__((address_space(3))) double* CoefPtr;
+constexpr int kCoefExp2 = 0;          // offset of the exp2 coefficients
+constexpr int kCoefLog2 = kExp2N;     // offset of the log2 coefficients
+constexpr int kCoefN = kExp2N + kLog2N;
+
 __device__ __forceinline__ double exp2_poly10(double f) {
-    double p = 0x1.e6063f7217bc6p-28;
-    p = __builtin_fma(p, f, 0x1.b675bca4eeebbp-24);
-    p = __builtin_fma(p, f, 0x1.62bfd47773353p-20);
-    p = __builtin_fma(p, f, 0x1.ffcb54062e698p-17);
-    p = __builtin_fma(p, f, 0x1.430913096fd9fp-13);
-    p = __builtin_fma(p, f, 0x1.5d87fe9d7a584p-10);
-    p = __builtin_fma(p, f, 0x1.3b2ab6fba1ddap-7);
-    p = __builtin_fma(p, f, 0x1.c6b08d703ce49p-5);
-    p = __builtin_fma(p, f, 0x1.ebfbdff82c598p-3);
-    p = __builtin_fma(p, f, 0x1.62e42fefa3a19p-1);
-    p = __builtin_fma(p, f, 1.0);
+    double p = kExp2C[0];
+#pragma unroll
+    for (int i = 1; i < kExp2N; ++i) p = __builtin_fma(p, f, kExp2C[i]);
+    return p;
+}
+__device__ __forceinline__ double exp2_poly10(double f, CoefPtr cf) {
+    double p = cf[kCoefExp2];
+#pragma unroll
+    for (int i = 1; i < kExp2N; ++i) p = __builtin_fma(p, f, cf[kCoefExp2 + i]);
     return p;
 }
 
@@ -197,6 +218,11 @@ __device__ __forceinline__ double exp2_full(double u) {
     double f = u - n;
     return __builtin_amdgcn_ldexp(exp2_poly10(f), cvt_i32_sat(n));
 }
+__device__ __forceinline__ double exp2_full(double u, CoefPtr cf) {
+    double n = __builtin_rint(u);
+    double f = u - n;
+    return __builtin_amdgcn_ldexp(exp2_poly10(f, cf), cvt_i32_sat(n));
+}
 
 // 1/b for finite normal b: hardware estimate plus two Newton steps.
 __device__ __forceinline__ double rcp_f64(double b) {
@@ -215,8 +241,10 @@ __device__ __forceinline__ double div_f64(double a, double b) {
 
 // log2(x) for finite x > 0 (normal or subnormal); also returns the rounding
 // error of the result in `lo` (hi + lo carries about 2^-104 relative of the
-// exponent part, within the polynomial's own error).
-__device__ __forceinline__ double log2_full_dd(double x, double& lo) {
+// exponent part, within the polynomial's own error). C: coefficient source
+// (kLog2C or an LDS copy).
+template <typename C>
+__device__ __forceinline__ double log2_dd_impl(double x, double& lo, C c) {
     int e = __builtin_amdgcn_frexp_exp(x);
     double m = __builtin_amdgcn_frexp_mant(x);  // [0.5, 1)
     if (m < 0x1.6a09e667f3bcdp-1) {             // sqrt(1/2)
@@ -225,27 +253,25 @@ __device__ __forceinline__ double log2_full_dd(double x, double& lo) {
     }
     const double u = div_f64(m - 1.0, m + 1.0);
     const double w = u * u;
-    double p = 0x1.00ecd7e080215p-3;
-    p = __builtin_fma(p, w, 0x1.1964ec6fc9491p-3);
-    p = __builtin_fma(p, w, 0x1.3703c1f4d0ffep-3);
-    p = __builtin_fma(p, w, 0x1.5b9ac9b743f0dp-3);
-    p = __builtin_fma(p, w, 0x1.89f3b1694cffep-3);
-    p = __builtin_fma(p, w, 0x1.c68f568d31760p-3);
-    p = __builtin_fma(p, w, 0x1.0c9a84994022dp-2);
-    p = __builtin_fma(p, w, 0x1.484b13d7c02a9p-2);
-    p = __builtin_fma(p, w, 0x1.a61762a7aded9p-2);
-    p = __builtin_fma(p, w, 0x1.2776c50ef9bfep-1);
-    p = __builtin_fma(p, w, 0x1.ec709dc3a03fdp-1);
-    p = __builtin_fma(p, w, 0x1.71547652b82fep+1);
+    double p = c[0];
+#pragma unroll
+    for (int i = 1; i < kLog2N; ++i) p = __builtin_fma(p, w, c[i]);
     const double ed = (double)e;
     const double hi = __builtin_fma(u, p, ed);
     lo = __builtin_fma(u, p, ed - hi);  // ed - hi is exact (|u p| <= 1/2)
     return hi;
 }
-
+__device__ __forceinline__ double log2_full_dd(double x, double& lo) { return log2_dd_impl(x, lo, kLog2C); }
+__device__ __forceinline__ double log2_full_dd(double x, double& lo, CoefPtr cf) {
+    return log2_dd_impl(x, lo, cf + kCoefLog2);
+}
 __device__ __forceinline__ double log2_full(double x) {
     double lo;
     return log2_full_dd(x, lo);
+}
+__device__ __forceinline__ double log2_full(double x, CoefPtr cf) {
+    double lo;
+    return log2_full_dd(x, lo, cf);
 }
 
 __device__ __forceinline__ float next_up(float x) {  // x >= 0 finite
@@ -370,7 +396,17 @@ struct alignas(16) LqEntry {
 struct ConstTables {
     LqEntry lqb[2][256];
     double lqm[2][128];
+    double coef[kCoefN];
 };
+
+// The coefficient copy, through a pointer the optimizer cannot see through
+// (so that per-tile code reloads the coefficients from LDS instead of hoisting
+// them into registers across the tile loop).
+__device__ __forceinline__ CoefPtr coef_ptr(const ConstTables& ct) {
+    uint32_t a = (uint32_t)(uintptr_t)(CoefPtr)ct.coef;
+    asm volatile("" : "+v"(a));
+    return (CoefPtr)(uintptr_t)a;
+}
 
 template <int F>
 __device__ double lq_entry(int c) {
@@ -409,6 +445,8 @@ __device__ __forceinline__ void fill_tables(ConstTables& ct, double bm, double b
     ct.lqb[f][c] = LqEntry{lq, b};
     ct.lqb[f][c | 128] = LqEntry{lq, -b};
     ct.lqm[f][c] = f ? lqm_entry<FV>(c) : lqm_entry<FM>(c);
+    if (threadIdx.x < kCoefN)
+        ct.coef[threadIdx.x] = threadIdx.x < kExp2N ? kExp2C[threadIdx.x] : kLog2C[threadIdx.x - kExp2N];
     __syncthreads();
 }
 
@@ -540,7 +578,7 @@ __device__ __forceinline__ NewGroup swap_pair(const NewGroup& g) {
 // k = 1 the expanded value is formed as fpmax (|x| / amax) with IEEE
 // operations; otherwise |x| is compared with amax 2^(log2(mid / fpmax) / k).
 __device__ __forceinline__ uint32_t exact_mag(double ax, uint32_t lo, const NewGroup& g, const double* lqm,
-                                              double mid, const FmtRT& F) {
+                                              double mid, const FmtRT& F, CoefPtr cf) {
     bool up;
     bool tie;
     if (g.k == 1.0f) {
@@ -548,7 +586,7 @@ __device__ __forceinline__ uint32_t exact_mag(double ax, uint32_t lo, const NewG
         up = y > mid;
         tie = y == mid;
     } else {
-        const double thr = g.amax * exp2_full(lqm[lo] * g.r);
+        const double thr = g.amax * exp2_full(lqm[lo] * g.r, cf);
         up = ax > thr;
         tie = ax == thr;
     }
@@ -560,14 +598,14 @@ __device__ __forceinline__ uint32_t exact_mag(double ax, uint32_t lo, const NewG
 // and the standalone quantizer's slow elements): y = fpmax (|x| / amax)^k in
 // fp64, formed as fpmax (|x| / amax) with IEEE operations when k = 1.
 template <int F>
-__device__ uint32_t exact_code_full(double x, const NewGroup& g) {
+__device__ uint32_t exact_code_full(double x, const NewGroup& g, CoefPtr cf) {
     using T = Fmt<F>;
     const uint32_t sign = __builtin_signbit(x) ? 0x80u : 0u;
     if (g.flags & kPoison) return 0x7Fu;
     if (x == 0.0 || g.amax == 0.0) return sign;
     const double t = __builtin_fabs(x) / g.amax;
     const double y = (g.k == 1.0f) ? T::FPMAX * t
-                                   : exp2_full((double)g.k * log2_full(t) + T::LOG2_FPMAX);
+                                   : exp2_full((double)g.k * log2_full(t, cf) + T::LOG2_FPMAX, cf);
     return sign | encode_mag_exact<F>(y);
 }
 
@@ -668,7 +706,7 @@ template <int F>
 __device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&codes)[4],
                                                const uint32_t (*old)[kWave], const Park& pk, int og_row,
                                                const NewGroup& ng, const LqEntry* lq, const double* lqm,
-                                               const FmtRT& F_, double cb, bool square) {
+                                               const FmtRT& F_, double cb, bool square, CoefPtr cf) {
     const int lane = threadIdx.x & (kWave - 1);
     const OldGroup og{pk.og[og_row][lane], pk.og[og_row + 1][lane], pk.og[og_row + 2][lane]};
     while (__any((amb[0] | amb[1] | amb[2] | amb[3]) != 0u)) {
@@ -687,10 +725,10 @@ __device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&co
             const uint32_t lo = byte_of(fastw, bi) & 0x7Fu;
             uint32_t code;
             if (ng.flags & kSlow) {
-                code = exact_code_full<F>(x, ng);
+                code = exact_code_full<F>(x, ng, cf);
             } else {
                 const double mid = 0.5 * (value_of<F>(lo) + value_of<F>(lo + 1));
-                code = (__builtin_signbit(x) ? 0x80u : 0u) | exact_mag(__builtin_fabs(x), lo, ng, lqm, mid, F_);
+                code = (__builtin_signbit(x) ? 0x80u : 0u) | exact_mag(__builtin_fabs(x), lo, ng, lqm, mid, F_, cf);
             }
             const uint32_t mask = ~(0xFFu << (8 * bi)), ins = code << (8 * bi);
             const uint32_t clear = ~(0x80u << (8 * bi));
@@ -826,6 +864,7 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     int odd_bit = lane & 1;
     asm volatile("" : "+v"(odd_bit));
     const bool odd = odd_bit != 0;
+    const CoefPtr cf = coef_ptr(ct);
     const FmtRT fm = fmt_rt<FM>(), fv = fmt_rt<FV>();
 
     gfloat* P = gp(t.p);
@@ -1013,8 +1052,8 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     if (nm.flags & kPoison) { am[0] = am[1] = am[2] = am[3] = 0u; }
     if (nv.flags & kPoison) { av[0] = av[1] = av[2] = av[3] = 0u; }
     if (__any((am[0] | am[1] | am[2] | am[3] | av[0] | av[1] | av[2] | av[3]) != 0u)) {
-        redo_ambiguous<FM>(am, cm, pk.mq, pk, 0, nm, lq_m, ct.lqm[0], fm, c.c1, false);
-        redo_ambiguous<FV>(av, cv, pk.vq, pk, 3, nv, lq_v, ct.lqm[1], fv, c.c2, true);
+        redo_ambiguous<FM>(am, cm, pk.mq, pk, 0, nm, lq_m, ct.lqm[0], fm, c.c1, false, cf);
+        redo_ambiguous<FV>(av, cv, pk.vq, pk, 3, nv, lq_v, ct.lqm[1], fv, c.c2, true, cf);
     }
     if (nm.flags & kPoison) { cm[0] = cm[1] = cm[2] = cm[3] = 0x7F7F7F7Fu; }
     if (nv.flags & kPoison) { cv[0] = cv[1] = cv[2] = cv[3] = 0x7F7F7F7Fu; }
@@ -1151,6 +1190,7 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
         amin = group_min(amin, lpg);
         const bool poison = group_or(bad ? 1u : 0u, lpg) != 0u;
         double la_lo, lb_lo;
+        const CoefPtr cf = coef_ptr(ct);
         const double la = log2_stat(amax, la_lo), lb = log2_stat(amin, lb_lo);
         const NewGroup ng = new_group(amax, amin, la, la_lo, lb, lb_lo, poison, expand, fr);
         uint32_t cw[4], amb[4];
@@ -1180,9 +1220,9 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
                 const uint32_t lo = byte_of(select4(wi, cw[0], cw[1], cw[2], cw[3]), bi) & 0x7Fu;
                 const double mid = 0.5 * (value_of<F>(lo) + value_of<F>(lo + 1));
                 const uint32_t code = (ng.flags & kSlow)
-                                          ? exact_code_full<F>(xd, ng)
+                                          ? exact_code_full<F>(xd, ng, cf)
                                           : ((__builtin_signbit(xd) ? 0x80u : 0u) |
-                                             exact_mag(__builtin_fabs(xd), lo, ng, ct.lqm[0], mid, fr));
+                                             exact_mag(__builtin_fabs(xd), lo, ng, ct.lqm[0], mid, fr, cf));
                 const uint32_t mask = ~(0xFFu << (8 * bi)), ins = code << (8 * bi);
                 const uint32_t clear = ~(0x80u << (8 * bi));
                 if (wi == 0) { cw[0] = (cw[0] & mask) | ins; amb[0] &= clear; }
