@@ -389,6 +389,27 @@ __device__ float decode_value(uint32_t code) {
 //            is b x; the codec kernels use b = 1);
 //   lqm[c] = log2(midpoint(c, c+1) / fpmax), the per-code constant of the
 //            exact requantization threshold.
+struct ExpJob {
+    double xh, xl;
+    int32_t slot;
+    int32_t te;  // 1: a TE entry (A = a, times the decay b); 0: a TS entry (and its negative)
+};
+struct ProdJob {
+    uint8_t src, pow, dst, neg;
+};
+struct TableJobs {
+    ExpJob e[12];
+    ProdJob p[28];
+};
+// One builder lane's share, in the form the builder consumes: three entries
+// fm 2^(fa a + r x) written to `slot` and negated to `nslot`, then seven
+// products table[src] * table[mul] written to `dst` and negated to `ndst`
+// (offsets in bytes; the trash slot where no negative is wanted).
+struct LaneJob {
+    double xh[3], xl[3], fa[3], fm[3];
+    uint32_t slot[3], nslot[3];
+    uint32_t src[7], mul[7], dst[7], ndst[7];
+};
 struct alignas(16) LqEntry {
     double lq;
     double b;
@@ -397,6 +418,10 @@ struct ConstTables {
     LqEntry lqb[2][256];
     double lqm[2][128];
     double coef[kCoefN];
+    uint32_t lut[2][256];  // per-group table offsets of each code (see GroupTable)
+    double lsi[16][2];     // log2(i), i = 0..15, as hi + lo
+    TableJobs jobs[2];     // how the lanes of a group build each moment's table
+    LaneJob lj[8];         // the same per builder lane (moment * 4 + lane in quad)
 };
 
 // The coefficient copy, through a pointer the optimizer cannot see through
@@ -435,6 +460,87 @@ __device__ double lqm_entry(int c) {
     return ((double)e - T::LOG2_FPMAX) + log2_full(__builtin_amdgcn_frexp_mant(mid));
 }
 
+// Per-group dequantization tables (groups of 128 and more, tiles inside the
+// tensor). A code's magnitude is 2^(max(e,1) - BIAS - MB) * i with e its
+// exponent field and i its integer significand (the mantissa field, plus
+// 2^MB when e > 0), so a group's dequantized, decay-scaled moment
+// b sign(q) (|q| s)^(1/k) = b 2^(a + r (max(e,1) - BIAS - MB - log2 fpmax)) * sign i^r
+// is the product of two table entries: TE[e] (32 slots, times b) and
+// TS[j], j = i + NEG * sign (32 slots). TE[31] holds NaN (E4M3: its NaN
+// code) or Inf (E5M2: e = 31); TS[31] holds NaN for E5M2's NaN codes.
+struct GroupTable {
+    // TE = v[0..31], TS = v[32..63], the powers (2^r)^0..3 at v[64..67], a
+    // trash slot v[68]; the odd size spreads the groups over the LDS banks
+    double v[69];
+};
+constexpr int kTsBase = 32;
+constexpr int kPowBase = 64;
+constexpr int kTrash = 68;
+template <int F>
+__device__ uint32_t lut_entry(int code) {
+    using T = Fmt<F>;
+    constexpr int NEG = 2 << T::MB;  // sign offset in TS
+    const int mag = code & 0x7F, e = mag >> T::MB, m = mag & ((1 << T::MB) - 1);
+    int te = e, ts = (e ? (m | (1 << T::MB)) : m) + ((code & 0x80) ? NEG : 0);
+    if (T::is_nan(mag)) {
+        te = 31;
+        if (F == COAT_FMT_E5M2) ts = 31;
+    }
+    const uint32_t te_off = (uint32_t)(te * 8);
+    const uint32_t ts_off = (uint32_t)((kTsBase + ts) * 8);
+    return te_off | (ts_off << 16);
+}
+
+// The work of building one moment's table, split over four lanes: 12 entries
+// evaluated as 2^(A + r x) (x = log2 i for TS[i], A = 0; x = max(e,1) - BIAS
+// - MB - log2 fpmax for TE[e], A = a), 3 per lane, then up to 28 products
+// table[dst] = table[src] * (2^r)^pow, 7 per lane. Entries:
+//   E4M3: TS[i], i in {2,3,5,7,9,11,13,15}; TE anchors {0,4,8,12};
+//   E5M2: TS[i], i in {2,3,5,7}; TE anchors {0,4,...,28}.
+// TS[2i] = TS[i] 2^r and TE[e + j] = TE[e] 2^(r j) for e >= 1 (TE[0] = TE[1],
+// so from the anchor 0 the powers start at 0). Unused product slots write a
+// trash entry that no code reads.
+template <int F>
+__device__ void table_jobs(TableJobs& j, int tid) {
+    using T = Fmt<F>;
+    constexpr bool E4 = F == COAT_FMT_E4M3;
+    constexpr int NTS = E4 ? 8 : 4;
+    constexpr int TRASH = E4 ? 16 : kTsBase + 16;  // E4M3 has no TE[16..30]; E5M2 no TS[16..30]
+    if (tid < 12) {
+        ExpJob& e = j.e[tid];
+        if (tid < NTS) {
+            const int ts[8] = {2, 3, 5, 7, 9, 11, 13, 15};
+            const int i = ts[tid];
+            e.xh = log2_full_dd((double)i, e.xl);
+            e.slot = kTsBase + i;
+            e.te = 0;
+        } else {
+            const int a = 4 * (tid - NTS);
+            const double x = (double)((a > 0 ? a : 1) - T::BIAS - T::MB);
+            const double h = x - T::LOG2_FPMAX;
+            const double bb = h - x;
+            e.xh = h;
+            e.xl = ((x - (h - bb)) + (-T::LOG2_FPMAX - bb)) - T::LOG2_FPMAX_LO;
+            e.slot = a;
+            e.te = 1;
+        }
+    } else if (tid < 12 + 28) {
+        const int q = tid - 12;
+        ProdJob pj{0, 0, (uint8_t)TRASH, 0};
+        // TS products first, then the TE chains
+        const int ts_src[6] = {2, 3, 2, 5, 3, 7}, ts_pow[6] = {1, 1, 2, 1, 2, 1}, ts_dst[6] = {4, 6, 8, 10, 12, 14};
+        const int nts = E4 ? 6 : 2;
+        const int nte = (E4 ? 4 : 8) * 3;
+        if (q < nts) {
+            pj = ProdJob{(uint8_t)(kTsBase + ts_src[q]), (uint8_t)ts_pow[q], (uint8_t)(kTsBase + ts_dst[q]), 1};
+        } else if (q < nts + nte) {
+            const int r = q - nts, a = 4 * (r / 3), jj = 1 + r % 3;
+            pj = ProdJob{(uint8_t)a, (uint8_t)(a == 0 ? jj - 1 : jj), (uint8_t)(a + jj), 0};
+        }
+        j.p[q] = pj;
+    }
+}
+
 // Filled by the block's 256 threads: thread i covers moment i >> 7, code i & 127
 // and its negative.
 template <int FM, int FV>
@@ -447,6 +553,40 @@ __device__ __forceinline__ void fill_tables(ConstTables& ct, double bm, double b
     ct.lqm[f][c] = f ? lqm_entry<FV>(c) : lqm_entry<FM>(c);
     if (threadIdx.x < kCoefN)
         ct.coef[threadIdx.x] = threadIdx.x < kExp2N ? kExp2C[threadIdx.x] : kLog2C[threadIdx.x - kExp2N];
+    ct.lut[f][c] = f ? lut_entry<FV>(c) : lut_entry<FM>(c);
+    ct.lut[f][c | 128] = f ? lut_entry<FV>(c | 128) : lut_entry<FM>(c | 128);
+    if (threadIdx.x < 64) table_jobs<FM>(ct.jobs[0], threadIdx.x);
+    else if (threadIdx.x < 128) table_jobs<FV>(ct.jobs[1], threadIdx.x - 64);
+    if (threadIdx.x < 16) {
+        double lo = 0.0;
+        const double hi = threadIdx.x > 0 ? log2_full_dd((double)threadIdx.x, lo) : 0.0;
+        ct.lsi[threadIdx.x][0] = hi;
+        ct.lsi[threadIdx.x][1] = lo;
+    }
+    __syncthreads();
+    if (threadIdx.x < 8) {
+        const int mu = threadIdx.x >> 2, t = threadIdx.x & 3;
+        const bool e4 = (mu ? FV : FM) == COAT_FMT_E4M3;
+        const uint32_t NEG = e4 ? 16 : 8;
+        const TableJobs& J = ct.jobs[mu];
+        LaneJob& L = ct.lj[threadIdx.x];
+        for (int q = 0; q < 3; ++q) {
+            const ExpJob& e = J.e[3 * t + q];
+            L.xh[q] = e.xh;
+            L.xl[q] = e.xl;
+            L.fa[q] = e.te ? 1.0 : 0.0;
+            L.fm[q] = e.te ? (mu ? bv : bm) : 1.0;
+            L.slot[q] = 8u * (uint32_t)e.slot;
+            L.nslot[q] = 8u * (e.te ? (uint32_t)kTrash : (uint32_t)e.slot + NEG);
+        }
+        for (int q = 0; q < 7; ++q) {
+            const ProdJob& pj = J.p[7 * t + q];
+            L.src[q] = 8u * pj.src;
+            L.mul[q] = 8u * (kPowBase + pj.pow);
+            L.dst[q] = 8u * pj.dst;
+            L.ndst[q] = 8u * (pj.neg ? (uint32_t)pj.dst + NEG : (uint32_t)kTrash);
+        }
+    }
     __syncthreads();
 }
 
@@ -461,12 +601,14 @@ struct OldGroup {
     double a;
     double a_lo;
     double r;
+    double r_lo;  // rounding error of r = 1/k (used by the per-group tables)
 };
 
 __device__ __forceinline__ OldGroup old_group(double s, float k, double log2_fpmax, double log2_fpmax_lo) {
     OldGroup g;
     const double kd = (double)k;
     g.r = rcp_f64(kd);
+    g.r_lo = __builtin_fma(-kd, g.r, 1.0) * g.r;
     g.a_lo = 0.0;
     if (s > 0.0 && s < __builtin_inf()) {
         double l_lo;
@@ -476,9 +618,8 @@ __device__ __forceinline__ OldGroup old_group(double s, float k, double log2_fpm
         const double bb = t - l;
         const double t_lo = ((l - (t - bb)) + (log2_fpmax - bb)) + (l_lo + log2_fpmax_lo);
         // (t + t_lo) * (r + r_lo), r_lo the rounding error of 1/k
-        const double r_lo = __builtin_fma(-kd, g.r, 1.0) * g.r;
         g.a = t * g.r;
-        g.a_lo = __builtin_fma(t, g.r, -g.a) + __builtin_fma(t, r_lo, t_lo * g.r);
+        g.a_lo = __builtin_fma(t, g.r, -g.a) + __builtin_fma(t, g.r_lo, t_lo * g.r);
     } else {
         g.a = (s == 0.0) ? -1e300 : __builtin_nan("");
     }
@@ -558,7 +699,7 @@ __device__ NewGroup new_group(double amax, double amin, double L, double L_lo, d
 
 // Swap the per-group results of a lane pair (lane ^ 1).
 __device__ __forceinline__ OldGroup swap_pair(const OldGroup& g) {
-    return OldGroup{dpp64<kDppXor1>(g.a), dpp64<kDppXor1>(g.a_lo), dpp64<kDppXor1>(g.r)};
+    return OldGroup{dpp64<kDppXor1>(g.a), dpp64<kDppXor1>(g.a_lo), dpp64<kDppXor1>(g.r), dpp64<kDppXor1>(g.r_lo)};
 }
 __device__ __forceinline__ NewGroup swap_pair(const NewGroup& g) {
     NewGroup o;
@@ -692,23 +833,24 @@ struct Park {
     uint32_t gw[8][kWave];
     uint32_t mq[4][kWave];
     uint32_t vq[4][kWave];
-    double og[6][kWave];  // m: a, a_lo, r; v: a, a_lo, r
+    double og[6][kWave];  // direct path: m: a, a_lo, r; v: a, a_lo, r
+    double s[2][kWave];   // table path: the stored scales as loaded (TileIn s0, s1)
+    float k[2][kWave];    // and exponents (k0, k1), from which the rare paths recompute them
 };
 
 // Exact decision for the elements whose fast code is flagged in `amb` (one
 // moment): the element's new moment is recomputed in fp64 exactly as in the
 // main pass (its old code, grad and the dequantization constants read back
-// from the park area; `old` is the moment's code rows, og_row its first
-// constant row), then rounded with the fp64 threshold (or from scratch for
+// from the park area; `old` is the moment's code rows, og the moment's
+// dequantization constants), then rounded with the fp64 threshold (or from scratch for
 // groups outside the fp32 path's range). Loops until no lane has a flagged
 // element.
 template <int F>
 __device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&codes)[4],
-                                               const uint32_t (*old)[kWave], const Park& pk, int og_row,
+                                               const uint32_t (*old)[kWave], const Park& pk, const OldGroup& og,
                                                const NewGroup& ng, const LqEntry* lq, const double* lqm,
                                                const FmtRT& F_, double cb, bool square, CoefPtr cf) {
     const int lane = threadIdx.x & (kWave - 1);
-    const OldGroup og{pk.og[og_row][lane], pk.og[og_row + 1][lane], pk.og[og_row + 2][lane]};
     while (__any((amb[0] | amb[1] | amb[2] | amb[3]) != 0u)) {
         if ((amb[0] | amb[1] | amb[2] | amb[3]) != 0u) {
             const int wi = amb[0] ? 0 : (amb[1] ? 1 : (amb[2] ? 2 : 3));
@@ -842,12 +984,108 @@ __device__ __forceinline__ void load_full_tile(const TensorRef& t, int64_t tile,
     in.k1 = 1.0f;
 }
 
+// Per-wave LDS: the group tables during the element pass, then the park area.
+union WaveLds {
+    GroupTable tbl[16];
+    Park pk;
+};
+
+// 2^(h + l) for a double-double exponent with |l| small.
+__device__ __forceinline__ double exp2_dd(double h, double l) {
+    const double n = __builtin_rint(h);
+    return __builtin_amdgcn_ldexp(exp2_poly10((h - n) + l), cvt_i32_sat(n));
+}
+
+// a + b = s + err exactly.
+__device__ __forceinline__ double two_sum(double a, double b, double& err) {
+    const double s = a + b;
+    const double bb = s - a;
+    err = (a - (s - bb)) + (b - bb);
+    return s;
+}
+
+// (A + r x) in double-double for x = xh + xl and r = rh + rl, A = ah + al.
+__device__ __forceinline__ void fma_dd(double ah, double al, double rh, double rl, double xh, double xl,
+                                       double& h, double& l) {
+    const double p = rh * xh;
+    const double pe = __builtin_fma(rh, xh, -p) + __builtin_fma(rh, xl, rl * xh);
+    h = ah + p;
+    const double bb = h - ah;
+    l = ((ah - (h - bb)) + (p - bb)) + (al + pe);
+}
+
+// Builds the group tables of this tile (groups of 8 lanes or more): lanes
+// 0..3 of each group build the first moment's table, lanes 4..7 the second's,
+// each taking its LaneJob. Every entry is a correctly rounded 2^(A + r x)
+// with a double-double exponent, or a product of at most three such values.
+template <int FM, int FV>
+__device__ __forceinline__ void build_tables(WaveLds& wl, const ConstTables& ct, const OldGroup& om,
+                                             const OldGroup& ov, int lpg) {
+    // opaque, so that the lane's job parameters are derived in each tile
+    // instead of being hoisted out of the tile loop into registers
+    int lane = threadIdx.x & (kWave - 1);
+    asm volatile("" : "+v"(lane));
+    const int l = lane & (lpg - 1);
+    if (l >= 8) return;
+    const int mu = l >> 2, t = l & 3;
+    char* gb = reinterpret_cast<char*>(&wl.tbl[(lane / lpg) * 2 + mu]);
+    auto at = [&](uint32_t off) -> double& { return *reinterpret_cast<double*>(gb + off); };
+    const double a = mu ? ov.a : om.a, a_lo = mu ? ov.a_lo : om.a_lo;
+    const double r = mu ? ov.r : om.r, r_lo = mu ? ov.r_lo : om.r_lo;
+    const LaneJob& J = ct.lj[l];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        double h, lo;
+        fma_dd(J.fa[q] * a, J.fa[q] * a_lo, r, r_lo, J.xh[q], J.xl[q], h, lo);
+        const double v = J.fm[q] * exp2_dd(h, lo);
+        at(J.slot[q]) = v;
+        at(J.nslot[q]) = -v;
+    }
+    asm volatile("" ::: "memory");
+    if (t == 0) {
+        const double P = at(8u * (kTsBase + 2));
+        at(8u * kPowBase) = 1.0;
+        at(8u * (kPowBase + 1)) = P;
+        at(8u * (kPowBase + 2)) = P * P;
+        at(8u * (kPowBase + 3)) = P * P * P;
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 7; ++q) {
+        const double v = at(J.src[q]) * at(J.mul[q]);
+        at(J.dst[q]) = v;
+        at(J.ndst[q]) = -v;
+    }
+    if (t == 3) {
+        const bool e4 = (mu ? FV : FM) == COAT_FMT_E4M3;
+        const int NEG = e4 ? 16 : 8;
+        double* g = reinterpret_cast<double*>(gb);
+        g[kTsBase] = 0.0;
+        g[kTsBase + NEG] = -0.0;
+        g[kTsBase + 1] = 1.0;
+        g[kTsBase + 1 + NEG] = -1.0;
+        g[31] = e4 ? __builtin_nan("") : __builtin_inf();
+        if (!e4) g[kTsBase + 31] = __builtin_nan("");
+    }
+    asm volatile("" ::: "memory");
+}
+
+// b sign(q) (|q| s)^(1/k) of byte i of code word w from the group's table.
+__device__ __forceinline__ double table_dequant(uint32_t w, int i, const uint32_t* lut, const GroupTable& g) {
+    const uint32_t e = lut[(w >> (8 * i)) & 0xFFu];
+    const char* base = reinterpret_cast<const char*>(&g);
+    return *reinterpret_cast<const double*>(base + (e & 0xFFFFu)) *
+           *reinterpret_cast<const double*>(base + (e >> 16));
+}
+
 // One wavefront tile of the step: elements [tile*1024, tile*1024 + 1024) of t,
 // inputs in `in`. FULL: every element lies in the tensor and the group work is
 // split over lane pairs (group >= 32), so no lane needs a bounds check.
-template <int FM, int FV, bool FULL>
+template <int FM, int FV, bool FULL, bool TAB>
 __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
-                                          const ConstTables& ct, Park& pk, TileIn& in) {
+                                          const ConstTables& ct, WaveLds& wl, TileIn& in) {
+    static_assert(!TAB || FULL, "tables only for whole tiles");
+    Park& pk = wl.pk;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
     const int64_t rem = t.n - e0;
@@ -875,18 +1113,31 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     const uint32_t (&mq)[4] = in.mq;
     const uint32_t (&vq)[4] = in.vq;
 
-    // ---- stored group state -> dequantization constants
+    // ---- stored group state -> dequantization constants (all lanes must be
+    // active: the pair split exchanges results between lanes)
+    auto groups_of = [&](double s0, float k0, double s1, float k1, OldGroup& gm, OldGroup& gv) {
+        if (pair) {
+            const OldGroup mine = old_group(s0, k0, odd ? fv.log2_fpmax : fm.log2_fpmax,
+                                            odd ? fv.log2_fpmax_lo : fm.log2_fpmax_lo);
+            const OldGroup other = swap_pair(mine);
+            gm = odd ? other : mine;
+            gv = odd ? mine : other;
+        } else {
+            gm = old_group(s0, k0, fm.log2_fpmax, fm.log2_fpmax_lo);
+            gv = old_group(s1, k1, fv.log2_fpmax, fv.log2_fpmax_lo);
+        }
+    };
+    // the same from the parked state (rare paths, after the element pass)
+    auto parked_groups = [&](OldGroup& gm, OldGroup& gv) {
+        if constexpr (TAB) {
+            groups_of(pk.s[0][lane], pk.k[0][lane], pk.s[1][lane], pk.k[1][lane], gm, gv);
+        } else {
+            gm = OldGroup{pk.og[0][lane], pk.og[1][lane], pk.og[2][lane], 0.0};
+            gv = OldGroup{pk.og[3][lane], pk.og[4][lane], pk.og[5][lane], 0.0};
+        }
+    };
     OldGroup om, ov;
-    if (pair) {
-        const OldGroup mine = old_group(in.s0, in.k0, odd ? fv.log2_fpmax : fm.log2_fpmax,
-                                        odd ? fv.log2_fpmax_lo : fm.log2_fpmax_lo);
-        const OldGroup other = swap_pair(mine);
-        om = odd ? other : mine;
-        ov = odd ? mine : other;
-    } else {
-        om = old_group(in.s0, in.k0, fm.log2_fpmax, fm.log2_fpmax_lo);
-        ov = old_group(in.s1, in.k1, fv.log2_fpmax, fv.log2_fpmax_lo);
-    }
+    groups_of(in.s0, in.k0, in.s1, in.k1, om, ov);
 
     // ---- per element: dequantize, moments, statistics, AdamW update
     const LqEntry* lq_m = ct.lqb[0];
@@ -895,24 +1146,45 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     double amax_m = 0.0, amin_m = __builtin_inf(), amax_v = 0.0, amin_v = __builtin_inf();
     // sum of xm * xv: not finite if any moment is infinite or NaN (or beyond fp32)
     float fin = 0.0f;
+    // upd(i, cg, cg2, m1, v1): the new moments of element i from c1 g and c2 g^2
+    auto element_pass = [&](auto upd_moments) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        double tbm, tbv;
-        const double m0 = dequant_mag(mq[i >> 2], i & 3, om, lq_m, tbm);
-        const double v0 = dequant_mag(vq[i >> 2], i & 3, ov, lq_v, tbv);
-        const double g = bf16_to_f64(gw[i >> 1], i & 1);
-        const double m1 = __builtin_fma(tbm, m0, c.c1 * g);
-        const double v1 = __builtin_fma(tbv, v0, c.c2 * (g * g));
-        amax_m = vmax_abs(amax_m, m1);
-        amin_m = vmin_abs(amin_m, m1);
-        amax_v = vmax_abs(amax_v, v1);
-        amin_v = vmin_abs(amin_v, v1);
-        xm[i] = (float)m1;
-        xv[i] = (float)v1;
-        fin = __builtin_fmaf(xm[i], xv[i], fin);
-        const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(xv[i]), c.ib2, c.eps);
-        const float upd = xm[i] * __builtin_amdgcn_rcpf(den);
-        p[i] = __builtin_fmaf(-c.ssz, upd, p[i] * c.decay);
+        for (int i = 0; i < 16; ++i) {
+            const double g = bf16_to_f64(gw[i >> 1], i & 1);
+            double m1, v1;
+            upd_moments(i, c.c1 * g, c.c2 * (g * g), m1, v1);
+            amax_m = vmax_abs(amax_m, m1);
+            amin_m = vmin_abs(amin_m, m1);
+            amax_v = vmax_abs(amax_v, v1);
+            amin_v = vmin_abs(amin_v, v1);
+            xm[i] = (float)m1;
+            xv[i] = (float)v1;
+            fin = __builtin_fmaf(xm[i], xv[i], fin);
+            const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(xv[i]), c.ib2, c.eps);
+            const float upd = xm[i] * __builtin_amdgcn_rcpf(den);
+            p[i] = __builtin_fmaf(-c.ssz, upd, p[i] * c.decay);
+            // bound the scheduler's look-ahead (register pressure)
+            if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if constexpr (TAB) {
+        // groups of 128 and more: per-group tables
+        build_tables<FM, FV>(wl, ct, om, ov, lpg);
+        const GroupTable& tm = wl.tbl[(lane / lpg) * 2];
+        const GroupTable& tv = wl.tbl[(lane / lpg) * 2 + 1];
+        element_pass([&](int i, double cg, double cg2, double& m1, double& v1) {
+            m1 = table_dequant(mq[i >> 2], i & 3, ct.lut[0], tm) + cg;
+            v1 = table_dequant(vq[i >> 2], i & 3, ct.lut[1], tv) + cg2;
+        });
+        asm volatile("" ::: "memory");  // the park area reuses the tables' LDS
+    } else {
+        element_pass([&](int i, double cg, double cg2, double& m1, double& v1) {
+            double tbm, tbv;
+            const double m0 = dequant_mag(mq[i >> 2], i & 3, om, lq_m, tbm);
+            const double v0 = dequant_mag(vq[i >> 2], i & 3, ov, lq_v, tbv);
+            m1 = __builtin_fma(tbm, m0, cg);
+            v1 = __builtin_fma(tbv, v0, cg2);
+        });
     }
     // A zero moment (the minimum is over nonzero members) or a non-finite one:
     // the statistics are redone exactly.
@@ -922,8 +1194,13 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     for (int i = 0; i < 8; ++i) pk.gw[i][lane] = gw[i];
 #pragma unroll
     for (int i = 0; i < 4; ++i) { pk.mq[i][lane] = mq[i]; pk.vq[i][lane] = vq[i]; }
-    pk.og[0][lane] = om.a; pk.og[1][lane] = om.a_lo; pk.og[2][lane] = om.r;
-    pk.og[3][lane] = ov.a; pk.og[4][lane] = ov.a_lo; pk.og[5][lane] = ov.r;
+    if constexpr (TAB) {
+        pk.s[0][lane] = in.s0; pk.s[1][lane] = in.s1;
+        pk.k[0][lane] = in.k0; pk.k[1][lane] = in.k1;
+    } else {
+        pk.og[0][lane] = om.a; pk.og[1][lane] = om.a_lo; pk.og[2][lane] = om.r;
+        pk.og[3][lane] = ov.a; pk.og[4][lane] = ov.a_lo; pk.og[5][lane] = ov.r;
+    }
     // later reads of the park area must come from LDS, not from registers
     asm volatile("" ::: "memory");
 
@@ -931,8 +1208,8 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     if (__any(special)) {
         // Rare: exact statistics with zeros excluded from the minimum and
         // non-finite moments flagged, from the parked inputs.
-        const OldGroup pm{pk.og[0][lane], pk.og[1][lane], pk.og[2][lane]};
-        const OldGroup pv{pk.og[3][lane], pk.og[4][lane], pk.og[5][lane]};
+        OldGroup pm, pv;
+        parked_groups(pm, pv);
         amax_m = 0.0; amin_m = __builtin_inf(); amax_v = 0.0; amin_v = __builtin_inf();
         for (int i = 0; i < 16; ++i) {
             const uint32_t wm = pk.mq[i >> 2][lane];
@@ -1052,8 +1329,10 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     if (nm.flags & kPoison) { am[0] = am[1] = am[2] = am[3] = 0u; }
     if (nv.flags & kPoison) { av[0] = av[1] = av[2] = av[3] = 0u; }
     if (__any((am[0] | am[1] | am[2] | am[3] | av[0] | av[1] | av[2] | av[3]) != 0u)) {
-        redo_ambiguous<FM>(am, cm, pk.mq, pk, 0, nm, lq_m, ct.lqm[0], fm, c.c1, false, cf);
-        redo_ambiguous<FV>(av, cv, pk.vq, pk, 3, nv, lq_v, ct.lqm[1], fv, c.c2, true, cf);
+        OldGroup pm, pv;
+        parked_groups(pm, pv);
+        redo_ambiguous<FM>(am, cm, pk.mq, pk, pm, nm, lq_m, ct.lqm[0], fm, c.c1, false, cf);
+        redo_ambiguous<FV>(av, cv, pk.vq, pk, pv, nv, lq_v, ct.lqm[1], fv, c.c2, true, cf);
     }
     if (nm.flags & kPoison) { cm[0] = cm[1] = cm[2] = cm[3] = 0x7F7F7F7Fu; }
     if (nv.flags & kPoison) { cv[0] = cv[1] = cv[2] = cv[3] = 0x7F7F7F7Fu; }
@@ -1077,30 +1356,43 @@ __device__ __forceinline__ int64_t wave_id() {
     return (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 }
 
-// Full tiles of one tensor, then its final partial tile (if any).
-template <int FM, int FV>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) void step_single_kernel(TensorRef t, StepConsts c) {
+// Which tiles a step kernel launch covers.
+constexpr int kPhaseFull = 1;     // tiles wholly inside their tensor
+constexpr int kPhasePartial = 2;  // last tiles that end inside their tensor
+// A step over one tensor. TAB (groups of 128 and more): the whole tiles with
+// per-group tables, and nothing else; otherwise the tiles of `phases` on the
+// direct path (group 16: every tile on the general path).
+template <int FM, int FV, bool TAB>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) void step_single_kernel(
+    TensorRef t, StepConsts c, int phases) {
     __shared__ ConstTables ct;
-    __shared__ Park parks[kWavesPerBlock];
-    Park& pk = parks[threadIdx.x / kWave];
+    __shared__ WaveLds wls[kWavesPerBlock];
+    WaveLds& wl = wls[threadIdx.x / kWave];
     fill_tables<FM, FV>(ct, c.b1, c.b2);
     const int64_t full = t.n / kTile;
     const int64_t tiles = (t.n + kTile - 1) / kTile;
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
-    int64_t first = 0;
+    int64_t first = 0, last = 0;
     if (c.lg2_group >= 5) {
-        for (int64_t tile = wave_id(); tile < full; tile += nw) {
-            TileIn in;
-            load_full_tile(t, tile, c.lg2_group, in);
-            step_tile<FM, FV, true>(t, tile, c, ct, pk, in);
+        if (phases & kPhaseFull) {
+            for (int64_t tile = wave_id(); tile < full; tile += nw) {
+                TileIn in;
+                load_full_tile(t, tile, c.lg2_group, in);
+                step_tile<FM, FV, true, TAB>(t, tile, c, ct, wl, in);
+            }
         }
         first = full;
+        if (phases & kPhasePartial) last = tiles;
+    } else {
+        last = tiles;
     }
-    // general path: remaining tiles (all of them for group 16)
-    for (int64_t tile = first + wave_id(); tile < tiles; tile += nw) {
-        TileIn in;
-        load_tile(t, tile, c.lg2_group, in);
-        step_tile<FM, FV, false>(t, tile, c, ct, pk, in);
+    if constexpr (!TAB) {
+        // general path: the partial tile (every tile for group 16)
+        for (int64_t tile = first + wave_id(); tile < last; tile += nw) {
+            TileIn in;
+            load_tile(t, tile, c.lg2_group, in);
+            step_tile<FM, FV, false, false>(t, tile, c, ct, wl, in);
+        }
     }
 }
 
@@ -1108,41 +1400,45 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) 
 // entries) and the list of tensors with a partial last tile live in device
 // workspace. Each wavefront strides over the global full-tile index space,
 // walking the prefix forward to find the tensor of its tile; then the partial
-// tiles take the general path.
-template <int FM, int FV>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) void step_multi_kernel(const TensorRef* __restrict__ ts,
-                                                            const int64_t* __restrict__ full_begin,
-                                                            const int32_t* __restrict__ partial, int count,
-                                                            int n_partial, StepConsts c) {
+// tiles take the general path. Phases and TAB as for the single kernel.
+template <int FM, int FV, bool TAB>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) void step_multi_kernel(
+    const TensorRef* __restrict__ ts, const int64_t* __restrict__ full_begin, const int32_t* __restrict__ partial,
+    int count, int n_partial, StepConsts c, int phases) {
     __shared__ ConstTables ct;
-    __shared__ Park parks[kWavesPerBlock];
-    Park& pk = parks[threadIdx.x / kWave];
+    __shared__ WaveLds wls[kWavesPerBlock];
+    WaveLds& wl = wls[threadIdx.x / kWave];
     fill_tables<FM, FV>(ct, c.b1, c.b2);
     const int64_t full = full_begin[count];
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
-    if (c.lg2_group >= 5) {
+    if (phases & kPhaseFull) {
         int cur = 0;
-        for (int64_t tile = wave_id(); tile < full; tile += nw) {
-            while (tile >= full_begin[cur + 1]) ++cur;
-            TileIn in;
-            load_full_tile(ts[cur], tile - full_begin[cur], c.lg2_group, in);
-            step_tile<FM, FV, true>(ts[cur], tile - full_begin[cur], c, ct, pk, in);
-        }
-    } else {
-        int cur = 0;
-        for (int64_t tile = wave_id(); tile < full; tile += nw) {
-            while (tile >= full_begin[cur + 1]) ++cur;
-            TileIn in;
-            load_tile(ts[cur], tile - full_begin[cur], c.lg2_group, in);
-            step_tile<FM, FV, false>(ts[cur], tile - full_begin[cur], c, ct, pk, in);
+        if (c.lg2_group >= 5) {
+            for (int64_t tile = wave_id(); tile < full; tile += nw) {
+                while (tile >= full_begin[cur + 1]) ++cur;
+                TileIn in;
+                load_full_tile(ts[cur], tile - full_begin[cur], c.lg2_group, in);
+                step_tile<FM, FV, true, TAB>(ts[cur], tile - full_begin[cur], c, ct, wl, in);
+            }
+        } else if constexpr (!TAB) {
+            for (int64_t tile = wave_id(); tile < full; tile += nw) {
+                while (tile >= full_begin[cur + 1]) ++cur;
+                TileIn in;
+                load_tile(ts[cur], tile - full_begin[cur], c.lg2_group, in);
+                step_tile<FM, FV, false, false>(ts[cur], tile - full_begin[cur], c, ct, wl, in);
+            }
         }
     }
-    for (int64_t i = wave_id(); i < n_partial; i += nw) {
-        const TensorRef& t = ts[partial[i]];
-        const int64_t tile = t.n / kTile;
-        TileIn in;
-        load_tile(t, tile, c.lg2_group, in);
-        step_tile<FM, FV, false>(t, tile, c, ct, pk, in);
+    if constexpr (!TAB) {
+        if (phases & kPhasePartial) {
+            for (int64_t i = wave_id(); i < n_partial; i += nw) {
+                const TensorRef& t = ts[partial[i]];
+                const int64_t tile = t.n / kTile;
+                TileIn in;
+                load_tile(t, tile, c.lg2_group, in);
+                step_tile<FM, FV, false, false>(t, tile, c, ct, wl, in);
+            }
+        }
     }
 }
 
@@ -1406,18 +1702,38 @@ int check_tensor(const TensorRef& t) {
 
 int launch_status() { return hipGetLastError() == hipSuccess ? COAT_OK : COAT_EHIP; }
 
+// Groups of 128 and more: the whole tiles run in the table kernel, then a
+// direct-path launch covers any partial tiles. Otherwise one direct-path launch.
 template <int FM, int FV>
 void launch_single(const TensorRef& t, const StepConsts& c, hipStream_t st) {
-    const int64_t tiles = (t.n + kTile - 1) / kTile;
-    hipLaunchKernelGGL((step_single_kernel<FM, FV>), dim3(grid_for(tiles, kStepBlocksPerCU)), dim3(kBlock),
-                       0, st, t, c);
+    const int64_t tiles = (t.n + kTile - 1) / kTile, full = t.n / kTile;
+    if (c.lg2_group >= 7) {
+        if (full > 0)
+            hipLaunchKernelGGL((step_single_kernel<FM, FV, true>), dim3(grid_for(full, kStepBlocksPerCU)),
+                               dim3(kBlock), 0, st, t, c, kPhaseFull);
+        if (tiles > full)
+            hipLaunchKernelGGL((step_single_kernel<FM, FV, false>), dim3(1), dim3(kBlock), 0, st, t, c,
+                               kPhasePartial);
+        return;
+    }
+    hipLaunchKernelGGL((step_single_kernel<FM, FV, false>), dim3(grid_for(tiles, kStepBlocksPerCU)), dim3(kBlock),
+                       0, st, t, c, kPhaseFull | kPhasePartial);
 }
 
 template <int FM, int FV>
 void launch_multi(const TensorRef* ts, const int64_t* fb, const int32_t* partial, int count, int n_partial,
-                  int64_t tiles, const StepConsts& c, hipStream_t st) {
-    hipLaunchKernelGGL((step_multi_kernel<FM, FV>), dim3(grid_for(tiles, kStepBlocksPerCU)), dim3(kBlock),
-                       0, st, ts, fb, partial, count, n_partial, c);
+                  int64_t tiles, int64_t full, const StepConsts& c, hipStream_t st) {
+    if (c.lg2_group >= 7) {
+        if (full > 0)
+            hipLaunchKernelGGL((step_multi_kernel<FM, FV, true>), dim3(grid_for(full, kStepBlocksPerCU)),
+                               dim3(kBlock), 0, st, ts, fb, partial, count, n_partial, c, kPhaseFull);
+        if (n_partial > 0)
+            hipLaunchKernelGGL((step_multi_kernel<FM, FV, false>), dim3(grid_for(n_partial, kStepBlocksPerCU)),
+                               dim3(kBlock), 0, st, ts, fb, partial, count, n_partial, c, kPhasePartial);
+        return;
+    }
+    hipLaunchKernelGGL((step_multi_kernel<FM, FV, false>), dim3(grid_for(tiles, kStepBlocksPerCU)), dim3(kBlock),
+                       0, st, ts, fb, partial, count, n_partial, c, kPhaseFull | kPhasePartial);
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1522,11 +1838,11 @@ int coat_fp8_adamw_step_planned(const coat_multi_plan* plan, int32_t group, int3
     const int32_t* dpt = reinterpret_cast<const int32_t*>(ws + desc_bytes + fb_bytes);
     const int fm = fmt_m & 0xFF, fv = fmt_v & 0xFF;
     const int count = plan->count, np = plan->n_partial;
-    const int64_t tiles = plan->tiles;
-    if (fm == COAT_FMT_E4M3 && fv == COAT_FMT_E4M3) launch_multi<COAT_FMT_E4M3, COAT_FMT_E4M3>(dts, dfb, dpt, count, np, tiles, c, st);
-    else if (fm == COAT_FMT_E4M3) launch_multi<COAT_FMT_E4M3, COAT_FMT_E5M2>(dts, dfb, dpt, count, np, tiles, c, st);
-    else if (fv == COAT_FMT_E4M3) launch_multi<COAT_FMT_E5M2, COAT_FMT_E4M3>(dts, dfb, dpt, count, np, tiles, c, st);
-    else launch_multi<COAT_FMT_E5M2, COAT_FMT_E5M2>(dts, dfb, dpt, count, np, tiles, c, st);
+    const int64_t tiles = plan->tiles, full = plan->tiles - plan->n_partial;
+    if (fm == COAT_FMT_E4M3 && fv == COAT_FMT_E4M3) launch_multi<COAT_FMT_E4M3, COAT_FMT_E4M3>(dts, dfb, dpt, count, np, tiles, full, c, st);
+    else if (fm == COAT_FMT_E4M3) launch_multi<COAT_FMT_E4M3, COAT_FMT_E5M2>(dts, dfb, dpt, count, np, tiles, full, c, st);
+    else if (fv == COAT_FMT_E4M3) launch_multi<COAT_FMT_E5M2, COAT_FMT_E4M3>(dts, dfb, dpt, count, np, tiles, full, c, st);
+    else launch_multi<COAT_FMT_E5M2, COAT_FMT_E5M2>(dts, dfb, dpt, count, np, tiles, full, c, st);
     return launch_status();
 }
 
