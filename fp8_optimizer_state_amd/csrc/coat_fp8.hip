@@ -1070,12 +1070,14 @@ __device__ __forceinline__ void build_tables(WaveLds& wl, const ConstTables& ct,
     asm volatile("" ::: "memory");
 }
 
-// b sign(q) (|q| s)^(1/k) of byte i of code word w from the group's table.
-__device__ __forceinline__ double table_dequant(uint32_t w, int i, const uint32_t* lut, const GroupTable& g) {
+// b sign(q) (|q| s)^(1/k) + add for byte i of code word w, the product of the
+// group's two table entries fused with the addition.
+__device__ __forceinline__ double table_dequant_fma(uint32_t w, int i, const uint32_t* lut, const GroupTable& g,
+                                                    double add) {
     const uint32_t e = lut[(w >> (8 * i)) & 0xFFu];
     const char* base = reinterpret_cast<const char*>(&g);
-    return *reinterpret_cast<const double*>(base + (e & 0xFFFFu)) *
-           *reinterpret_cast<const double*>(base + (e >> 16));
+    return __builtin_fma(*reinterpret_cast<const double*>(base + (e & 0xFFFFu)),
+                         *reinterpret_cast<const double*>(base + (e >> 16)), add);
 }
 
 // One wavefront tile of the step: elements [tile*1024, tile*1024 + 1024) of t,
@@ -1173,8 +1175,8 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
         const GroupTable& tm = wl.tbl[(lane / lpg) * 2];
         const GroupTable& tv = wl.tbl[(lane / lpg) * 2 + 1];
         element_pass([&](int i, double cg, double cg2, double& m1, double& v1) {
-            m1 = table_dequant(mq[i >> 2], i & 3, ct.lut[0], tm) + cg;
-            v1 = table_dequant(vq[i >> 2], i & 3, ct.lut[1], tv) + cg2;
+            m1 = table_dequant_fma(mq[i >> 2], i & 3, ct.lut[0], tm, cg);
+            v1 = table_dequant_fma(vq[i >> 2], i & 3, ct.lut[1], tv, cg2);
         });
         asm volatile("" ::: "memory");  // the park area reuses the tables' LDS
     } else {
