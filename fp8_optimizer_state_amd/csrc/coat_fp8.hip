@@ -1165,8 +1165,6 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
             const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(xv[i]), c.ib2, c.eps);
             const float upd = xm[i] * __builtin_amdgcn_rcpf(den);
             p[i] = __builtin_fmaf(-c.ssz, upd, p[i] * c.decay);
-            // bound the scheduler's look-ahead (register pressure)
-            if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
     };
     if constexpr (TAB) {
@@ -1664,7 +1662,10 @@ unsigned grid_for(int64_t waves, int per_cu) {
     return (unsigned)(b < 1 ? 1 : b);
 }
 
-constexpr int kStepBlocksPerCU = 8;
+// Many more blocks than fit on a CU at once (3 here): blocks are handed to CUs
+// as earlier ones finish, which evens out the load across CUs and XCDs; beyond
+// about a hundred per CU each block's table set-up starts to cost more.
+constexpr int kStepBlocksPerCU = 128;
 
 bool finite_f(float x) { return x == x && x - x == 0.0f; }
 
