@@ -8,6 +8,11 @@ whole list. Prints one JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama13b]
                   [--no-cpu-baseline] [--copy-calibration]
+
+With --sweep it instead times the step and measures the state codec's
+quantization error for every group size in {32, 64, 128, 256}, format pair
+{E4M3/E4M3, E4M3/E5M2} and expansion on/off, on the same parameter list:
+one JSON line per variant on stdout, a markdown table on stderr.
 """
 from __future__ import annotations
 
@@ -47,6 +52,106 @@ def load_traffic(workload: str, n_launch_bytes: float):
     if pmc.get("source_sha256") != kernel_source_hash() or pmc.get("workload") != workload:
         return None
     return pmc.get("hbm_bytes_per_launch")
+
+
+def quant_error_sums(x, xhat, G: int):
+    """Quantization error of one tensor, as sums to pool over tensors:
+    (sum over groups with a nonzero norm of ||xhat - x||_2 / ||x||_2, number of
+    such groups, sum over nonzero x of |xhat - x| / |x|, number of nonzero x).
+    Groups are G consecutive elements; a short last group is padded with zeros,
+    which add to neither norm. Accumulated in fp64."""
+    import torch
+
+    x = x.reshape(-1).to(torch.float64)
+    d = xhat.reshape(-1).to(torch.float64) - x
+    pad = (-x.numel()) % G
+    if pad:
+        x = torch.nn.functional.pad(x, (0, pad))
+        d = torch.nn.functional.pad(d, (0, pad))
+    nx = x.view(-1, G).pow(2).sum(1).sqrt()
+    nd = d.view(-1, G).pow(2).sum(1).sqrt()
+    live = nx > 0
+    nz = x != 0
+    return (float((nd[live] / nx[live]).sum()), int(live.sum()),
+            float((d[nz].abs() / x[nz].abs()).sum()), int(nz.sum()))
+
+
+def sweep(args) -> int:
+    """Step time and codec error for each group size x format pair x expansion."""
+    import torch
+
+    import fp8_optimizer_state_amd as coat
+    import synth
+
+    base = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    coat.lib()
+    h = synth.HYPER
+    names = {0: "E4M3", 1: "E5M2"}
+    rows = []
+    for G in (32, 64, 128, 256):
+        st = coat.ParamListState(base.sizes, G, device=dev)
+        n = st.n_params
+        for fm, fv in ((0, 0), (0, 1)):
+            for expand in (True, False):
+                flag = 0 if expand else coat.FMT_NO_EXPAND
+                err = {"m": [0.0, 0, 0.0, 0], "v": [0.0, 0, 0.0, 0]}
+                for i, ni in enumerate(base.sizes):
+                    t = st.tensor(i)
+                    synth.params(ni, base.seed, i, device=dev, out=t.params)
+                    synth.grads(ni, base.seed, i, device=dev, out=t.grads)
+                    m, v = synth.prior_moments(ni, G, base.seed, i, device=dev)
+                    for name, x, q, s_, k_, f in (("m", m, t.m_q, t.m_s, t.m_k, fm), ("v", v, t.v_q, t.v_s, t.v_k, fv)):
+                        coat.quantize(x, q, s_, k_, group=G, fmt=f | flag)
+                        xh = torch.empty_like(x)
+                        coat.dequantize(q, s_, k_, xh, group=G, fmt=f)
+                        e = quant_error_sums(x, xh, G)
+                        acc = err[name]
+                        for j in range(4):
+                            acc[j] += e[j]
+                        del xh
+                    del m, v
+                torch.cuda.synchronize()
+                hy = dict(fmt_m=fm | flag, fmt_v=fv | flag, lr=h["lr"], beta1=h["b1"], beta2=h["b2"],
+                          eps=h["eps"], weight_decay=h["wd"])
+                st.plan()
+                step = h["step"]
+                for _ in range(args.warmup):
+                    st.step(step=step, **hy)
+                    step += 1
+                stream = torch.cuda.current_stream()
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                ev0.record(stream)
+                for _ in range(args.steps):
+                    st.step(step=step, **hy)
+                    step += 1
+                ev1.record(stream)
+                torch.cuda.synchronize()
+                ms = ev0.elapsed_time(ev1) / args.steps
+                bpp = 16.0 + 48.0 / G
+                gbps = bpp * n / (ms * 1e-3) / 1e9
+                row = {"sweep": args.workload, "group": G, "fmt_m": names[fm], "fmt_v": names[fv],
+                       "expand": expand, "n_params": n, "ms_per_step": ms, "params_per_s": n / (ms * 1e-3),
+                       "bytes_per_param": bpp, "achieved_GBps": gbps, "frac_of_8TBps": gbps / PEAK_HBM_GBPS,
+                       "m_err_normwise": err["m"][0] / err["m"][1], "m_err_elementwise": err["m"][2] / err["m"][3],
+                       "v_err_normwise": err["v"][0] / err["v"][1], "v_err_elementwise": err["v"][2] / err["v"][3]}
+                rows.append(row)
+                print(json.dumps(row), flush=True)
+                log(f"G={G} {names[fm]}/{names[fv]} expand={expand}: {ms:.2f} ms/step, "
+                    f"m err {row['m_err_normwise']:.4g}, v err {row['v_err_normwise']:.4g}")
+        del st
+        torch.cuda.empty_cache()
+    log("| G | m / v | expansion | ms/step | params/s | GB/s | % of 8 TB/s | m err (normwise) | m err (elem.) "
+        "| v err (normwise) | v err (elem.) |")
+    log("|---|---|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        log(f"| {r['group']} | {r['fmt_m']} / {r['fmt_v']} | {'on' if r['expand'] else 'off'} | "
+            f"{r['ms_per_step']:.2f} | {r['params_per_s']:.3e} | {r['achieved_GBps']:.0f} | "
+            f"{100 * r['frac_of_8TBps']:.1f} | {r['m_err_normwise']:.4g} | {r['m_err_elementwise']:.4g} | "
+            f"{r['v_err_normwise']:.4g} | {r['v_err_elementwise']:.4g} |")
+    return 0
 
 
 def cpu_baseline(wl, per_tensor: int = 229376) -> dict:
@@ -103,12 +208,16 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time and measure the codec error of every group size / format / expansion variant")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the step shards by whole groups with no exchange; see the design notes)",
               file=sys.stderr)
         return 2
+    if args.sweep:
+        return sweep(args)
 
     import torch
 
