@@ -66,6 +66,10 @@ def lib():
         L.coat_oracle_adamw_step.argtypes = [P, P, P, P, P, P, P, P, P, i64, i32, i32, i32,
                                              f32, f32, f32, f32, f32, i64]
         L.coat_oracle_adamw_step.restype = ctypes.c_int
+        L.coat_oracle_act_quantize.argtypes = [P, i64, i32, i32, P, P]
+        L.coat_oracle_act_quantize.restype = ctypes.c_int
+        L.coat_oracle_act_dequantize.argtypes = [P, P, i64, i32, i32, P]
+        L.coat_oracle_act_dequantize.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -130,6 +134,29 @@ def dequantize(q: np.ndarray, s: np.ndarray, k: np.ndarray, G: int, fmt: int) ->
     assert s.size == ngroups(q.size, G) and k.size == s.size
     x = np.empty(q.size, np.float64)
     _check(lib().coat_oracle_dequantize(_ptr(q), _ptr(s), _ptr(k), q.size, G, fmt, _ptr(x)))
+    return x
+
+
+# ---------------------------------------------------------------- activation codec
+
+def act_quantize(x: np.ndarray, G: int, fmt: int):
+    """bf16 values (as uint16 bits) to FP8 codes with absmax scaling, one fp32
+    scale per tensor (G = 0) or per group of G; returns (q uint8, s float32)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16).ravel()
+    n = x.size
+    q = np.empty(n, np.uint8)
+    s = np.empty(1 if G == 0 else ngroups(n, G), np.float32)
+    _check(lib().coat_oracle_act_quantize(_ptr(x), n, G, fmt, _ptr(q), _ptr(s)))
+    return q, s
+
+
+def act_dequantize(q: np.ndarray, s: np.ndarray, G: int, fmt: int) -> np.ndarray:
+    """FP8 codes and scales back to bf16 (uint16 bits)."""
+    q = np.ascontiguousarray(q, dtype=np.uint8).ravel()
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    assert s.size == (1 if G == 0 else ngroups(q.size, G))
+    x = np.empty(q.size, np.uint16)
+    _check(lib().coat_oracle_act_dequantize(_ptr(q), _ptr(s), q.size, G, fmt, _ptr(x)))
     return x
 
 

@@ -328,3 +328,78 @@ int coat_oracle_adamw_step(float* p, uint16_t* w, const uint16_t* g, uint8_t* m_
     free(v);
     return ORACLE_OK;
 }
+
+/* ---------------------------------------------------------------------- */
+/* FP8 activation codec, per tensor or per group                           */
+/* ---------------------------------------------------------------------- */
+/*
+ * Article, section "Solution: mixed-granularity FP8 precision flow": the
+ * inputs of linear and non-linear layers are kept in FP8 for the backward pass,
+ * and the quantization granularity differs between layers. The page gives no
+ * formula. Readings: plain absmax scaling (expansion is described for the
+ * optimizer states only); one fp32 scale per tensor (G = 0) or per group of G
+ * consecutive elements; bf16 values in and out:
+ *   s = RN32(amax / fpmax), amax = max |x| over the tensor or group;
+ *   code = encode(RN32(x / s)) if s > 0, else the sign of x alone (all-zero
+ *   groups, or amax so small that s underflows to 0);
+ *   a tensor or group holding a NaN or Inf: s = NaN and every code 0x7F;
+ *   dequantize: RN_bf16(RN32(value(code) * s)).
+ * RN32 of an fp64 quotient or product of these operands equals the fp32
+ * operation itself: fp64 carries more than 2*24 + 2 bits, so rounding twice is
+ * the same as rounding once.
+ */
+static void act_quantize_block(const uint16_t* x, int64_t len, int32_t fmt, uint8_t* q, float* s_out) {
+    double amax = 0.0;
+    int bad = 0;
+    for (int64_t i = 0; i < len; ++i) {
+        double v = bf16_to_double(x[i]);
+        if (!isfinite(v)) bad = 1;
+        else if (fabs(v) > amax) amax = fabs(v);
+    }
+    if (bad) {
+        *s_out = NAN;
+        for (int64_t i = 0; i < len; ++i) q[i] = 0x7F;
+        return;
+    }
+    float s = (float)(amax / fmt_fpmax(fmt));
+    *s_out = s;
+    for (int64_t i = 0; i < len; ++i) {
+        double v = bf16_to_double(x[i]);
+        if (s == 0.0f) {
+            q[i] = signbit(v) ? 0x80 : 0x00;
+            continue;
+        }
+        float y = (float)(v / (double)s);
+        q[i] = coat_oracle_fp8_encode((double)y, fmt);
+    }
+}
+
+static int check_act_args(int64_t n, int32_t G, int32_t fmt) {
+    if (n < 0 || G < 0 || (fmt != FMT_E4M3 && fmt != FMT_E5M2)) return ORACLE_EINVAL;
+    return ORACLE_OK;
+}
+
+/* G = 0: one scale for the whole array (s[0]); else one per group of G. */
+int coat_oracle_act_quantize(const uint16_t* x, int64_t n, int32_t G, int32_t fmt, uint8_t* q, float* s) {
+    if (check_act_args(n, G, fmt)) return ORACLE_EINVAL;
+    if (G == 0) {
+        act_quantize_block(x, n, fmt, q, s);
+        return ORACLE_OK;
+    }
+    for (int64_t g0 = 0, gi = 0; g0 < n; g0 += G, ++gi) {
+        int64_t len = (n - g0 < G) ? n - g0 : G;
+        act_quantize_block(x + g0, len, fmt, q + g0, s + gi);
+    }
+    return ORACLE_OK;
+}
+
+int coat_oracle_act_dequantize(const uint8_t* q, const float* s, int64_t n, int32_t G, int32_t fmt,
+                               uint16_t* x) {
+    if (check_act_args(n, G, fmt)) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i) {
+        float si = s[G == 0 ? 0 : i / G];
+        float p = (float)(coat_oracle_fp8_decode(q[i], fmt) * (double)si);
+        x[i] = float_to_bf16(p);
+    }
+    return ORACLE_OK;
+}
