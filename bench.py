@@ -13,6 +13,10 @@ With --sweep it instead times the step and measures the state codec's
 quantization error for every group size in {32, 64, 128, 256}, format pair
 {E4M3/E4M3, E4M3/E5M2} and expansion on/off, on the same parameter list:
 one JSON line per variant on stdout, a markdown table on stderr.
+
+With --act it times the FP8 activation codec (per tensor and per group of 128,
+E4M3 and E5M2) on a 16384 x 13824 bf16 activation matrix (the input of
+Llama-2-13B's down projection for 16k tokens): one JSON line per launch kind.
 """
 from __future__ import annotations
 
@@ -154,6 +158,49 @@ def sweep(args) -> int:
     return 0
 
 
+def act_bench(args) -> int:
+    """Throughput of the activation codec's entry points, inputs resident in HBM."""
+    import torch
+
+    import fp8_optimizer_state_amd as coat
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    coat.lib()
+    tokens, channels = 16384, 13824
+    x = synth.activations(tokens, channels, seed=13, device=dev)
+    n = x.numel()
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    back = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    for fmt, fname in ((0, "E4M3"), (1, "E5M2")):
+        for G in (0, 128):
+            s = torch.empty(coat.act_nscales(n, G), dtype=torch.float32, device=dev)
+            ops = (("quantize", lambda: coat.act_quantize(x, q, s, group=G, fmt=fmt),
+                    (2.0 + 2.0 + 1.0) if G == 0 else (2.0 + 1.0 + 4.0 / G)),
+                   ("dequantize", lambda: coat.act_dequantize(q, s, back, group=G, fmt=fmt),
+                    (1.0 + 2.0) if G == 0 else (1.0 + 4.0 / G + 2.0)))
+            for name, fn, bpe in ops:
+                for _ in range(args.warmup):
+                    fn()
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                ev0.record(stream)
+                for _ in range(args.steps):
+                    fn()
+                ev1.record(stream)
+                torch.cuda.synchronize()
+                ms = ev0.elapsed_time(ev1) / args.steps
+                gbps = bpe * n / (ms * 1e-3) / 1e9
+                row = {"act_codec": name, "granularity": "tensor" if G == 0 else f"group {G}", "fmt": fname,
+                       "n": n, "shape": [tokens, channels], "ms": ms, "elements_per_s": n / (ms * 1e-3),
+                       "bytes_per_element": bpe, "achieved_GBps": gbps, "frac_of_8TBps": gbps / PEAK_HBM_GBPS}
+                print(json.dumps(row), flush=True)
+                log(f"act {name} {row['granularity']} {fname}: {ms:.3f} ms, {gbps:.0f} GB/s")
+    return 0
+
+
 def cpu_baseline(wl, per_tensor: int = 229376) -> dict:
     """The oracle, single-threaded, on a bounded sample of the workload: the
     first `per_tensor` elements of every tensor (about 65M params for the
@@ -210,6 +257,7 @@ def main() -> int:
                     help="also run a plain device copy of known size (for counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="time and measure the codec error of every group size / format / expansion variant")
+    ap.add_argument("--act", action="store_true", help="time the FP8 activation codec instead of the step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -218,6 +266,8 @@ def main() -> int:
         return 2
     if args.sweep:
         return sweep(args)
+    if args.act:
+        return act_bench(args)
 
     import torch
 

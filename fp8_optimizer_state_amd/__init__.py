@@ -73,12 +73,15 @@ def lib() -> ctypes.CDLL:
     L.coat_fp8_dequantize.argtypes = [P, P, P, i64, i32, i32, P, P]
     L.coat_fp8_encode.argtypes = [P, i64, i32, P, P]
     L.coat_fp8_decode.argtypes = [P, i64, i32, P, P]
+    L.coat_fp8_act_quantize.argtypes = [P, i64, i32, i32, P, P, P]
+    L.coat_fp8_act_dequantize.argtypes = [P, P, i64, i32, i32, P, P]
     L.coat_strerror.argtypes = [ctypes.c_int]
     L.coat_strerror.restype = ctypes.c_char_p
     L.coat_abi_version.restype = ctypes.c_int
     for name in ("coat_fp8_adamw_step", "coat_multi_plan_init", "coat_fp8_adamw_step_planned",
                  "coat_fp8_adamw_step_multi", "coat_fp8_quantize", "coat_fp8_dequantize",
-                 "coat_fp8_encode", "coat_fp8_decode"):
+                 "coat_fp8_encode", "coat_fp8_decode", "coat_fp8_act_quantize",
+                 "coat_fp8_act_dequantize"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -168,6 +171,30 @@ def decode(q, y, *, fmt: int, stream=None) -> None:
     rc = lib().coat_fp8_decode(_ptr(q, torch.uint8, n, "q"), n, fmt,
                                _ptr(y, torch.float32, n, "y"), _stream(stream))
     _check(rc, "coat_fp8_decode")
+
+
+def act_nscales(n: int, group: int) -> int:
+    """Scales of an activation tensor: one per tensor (group 0) or per group."""
+    return 1 if group == 0 else ngroups(n, group)
+
+
+def act_quantize(x, q, scale, *, group: int, fmt: int, stream=None) -> None:
+    """bf16 activations -> FP8 codes + fp32 scales, per tensor (group 0) or per group."""
+    n = x.numel()
+    rc = lib().coat_fp8_act_quantize(_ptr(x, torch.bfloat16, n, "x"), n, group, fmt,
+                                     _ptr(q, torch.uint8, n, "q"),
+                                     _ptr(scale, torch.float32, act_nscales(n, group), "scale"),
+                                     _stream(stream))
+    _check(rc, "coat_fp8_act_quantize")
+
+
+def act_dequantize(q, scale, x, *, group: int, fmt: int, stream=None) -> None:
+    """FP8 codes + fp32 scales -> bf16 activations."""
+    n = q.numel()
+    rc = lib().coat_fp8_act_dequantize(_ptr(q, torch.uint8, n, "q"),
+                                       _ptr(scale, torch.float32, act_nscales(n, group), "scale"), n,
+                                       group, fmt, _ptr(x, torch.bfloat16, n, "x"), _stream(stream))
+    _check(rc, "coat_fp8_act_dequantize")
 
 
 # ---------------------------------------------------------------- parameter lists

@@ -170,6 +170,30 @@ int coat_fp8_dequantize(const uint8_t* q, const double* s, const float* k, int64
 int coat_fp8_encode(const float* y, int64_t n, int32_t fmt, uint8_t* q, coat_stream_t stream);
 int coat_fp8_decode(const uint8_t* q, int64_t n, int32_t fmt, float* y, coat_stream_t stream);
 
+/*
+ * FP8 activation codec with per-tensor or per-group granularity (article
+ * section "Solution: mixed-granularity FP8 precision flow": layer inputs are
+ * kept in FP8 for the backward pass, the quantization granularity varying
+ * between layers; which layer takes which granularity is the caller's
+ * choice). Plain absmax scaling of bf16 values, no expansion:
+ *   group == 0: one scale for the whole array (scale[1]);
+ *   group = G, a power of two in [16, 1024]: one scale per G consecutive
+ *   values (scale[ceil(n/G)], the last group may be short);
+ *   s = RN32(amax / fpmax); code = encode(RN32(x / s)) rounded to nearest,
+ *   ties to even, saturating (for s = 0, an all-zero group, the sign alone);
+ *   a tensor or group holding a NaN or Inf: s = NaN and every code 0x7F.
+ * Dequantize writes RN_bf16(RN32(decode(code) * s)).
+ *   x bf16 in (n), q out (n), scale out; fmt COAT_FMT_E4M3 or COAT_FMT_E5M2
+ *   (no flags). x, q 16-byte aligned (COAT_EALIGN), scale 4-byte aligned.
+ * Per tensor, the quantizer uses scale[0] as its accumulator while it runs
+ * (it enqueues four small launches); the caller must not read it until the
+ * stream reaches the end of the call.
+ */
+int coat_fp8_act_quantize(const uint16_t* x, int64_t n, int32_t group, int32_t fmt, uint8_t* q,
+                          float* scale, coat_stream_t stream);
+int coat_fp8_act_dequantize(const uint8_t* q, const float* scale, int64_t n, int32_t group,
+                            int32_t fmt, uint16_t* x, coat_stream_t stream);
+
 /* Static description of a status code. */
 const char* coat_strerror(int status);
 

@@ -15,6 +15,11 @@ Distributions (the workload recipe):
     The 1000:1 and 10:1 group ratios are the ones the COAT article reports
     for the first and second moments (section "FP8 optimizer states").
   * hyperparameters lr=1e-4, betas=(0.9, 0.95), eps=1e-8, wd=0.1, step=10.
+  * activations (for the FP8 activation codec), a (tokens, channels) bf16
+    matrix: N(0, 1) times a per-channel scale 10^U(-3, 1), and one value in a
+    thousand 50x larger (outliers), rounded to bf16. Stand-in for the inputs of
+    Llama-2-13B's linear layers (channels 5120 or 13824); the article gives no
+    activation statistics.
 
 Draws use ``torch.Generator`` on the device the tensors live on, one
 generator per (seed, tensor index, stream), so any tensor can be regenerated
@@ -128,6 +133,7 @@ WORKLOADS = {
 # ------------------------------------------------------------------ draws
 
 _STREAM_P, _STREAM_G, _STREAM_M, _STREAM_V, _STREAM_SG = 1, 2, 3, 4, 5
+_STREAM_ACT = 6
 
 
 def generator(seed: int, tensor: int, stream: int, device) -> torch.Generator:
@@ -153,6 +159,17 @@ def grads(n: int, seed: int, tensor: int = 0, device="cpu", out=None, step_index
         return g32.to(torch.bfloat16)
     out.copy_(g32)
     return out
+
+
+def activations(tokens: int, channels: int, seed: int, device="cpu") -> torch.Tensor:
+    """bf16 activations of shape (tokens, channels), flattened row-major."""
+    gen = generator(seed, channels, _STREAM_ACT, device)
+    ch = torch.empty(channels, dtype=torch.float32, device=device).uniform_(-3.0, 1.0, generator=gen)
+    x = torch.empty(tokens, channels, dtype=torch.float32, device=device).normal_(0.0, 1.0, generator=gen)
+    x.mul_(torch.pow(10.0, ch))
+    out = torch.empty(tokens, channels, dtype=torch.float32, device=device).uniform_(0.0, 1.0, generator=gen)
+    x = torch.where(out < 1e-3, x * 50.0, x)
+    return x.to(torch.bfloat16).reshape(-1)
 
 
 def prior_moments(n: int, G: int, seed: int, tensor: int = 0, device="cpu"):

@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
     for want in ("coat_fp8_adamw_step", "coat_fp8_adamw_step_multi", "coat_multi_plan_init",
                  "coat_fp8_adamw_step_planned", "coat_multi_workspace_bytes", "coat_fp8_quantize",
                  "coat_fp8_dequantize", "coat_fp8_encode", "coat_fp8_decode", "coat_strerror",
-                 "coat_abi_version"):
+                 "coat_abi_version", "coat_fp8_act_quantize", "coat_fp8_act_dequantize"):
         assert want in names
 
 
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_static_helpers():
     L = coat.lib()
-    assert L.coat_abi_version() == 101
+    assert L.coat_abi_version() == 102
     assert coat.strerror(0) == "ok" and "invalid" in coat.strerror(-1)
     assert L.coat_multi_workspace_bytes(363) >= 363 * 80 + 364 * 8
     assert L.coat_multi_workspace_bytes(363) % 256 == 0
@@ -89,6 +89,24 @@ def test_codec_argument_checks():
     assert L.coat_fp8_encode(FAKE, 10, 0x100, FAKE, None) == coat.COAT_EINVAL
     assert L.coat_fp8_decode(None, 10, 0, FAKE, None) == coat.COAT_EINVAL
     assert L.coat_fp8_encode(FAKE, 0, 0, None, None) == coat.COAT_OK
+
+
+def test_act_codec_argument_checks():
+    L = coat.lib()
+    q, d = L.coat_fp8_act_quantize, L.coat_fp8_act_dequantize
+    assert q(FAKE, 100, 96, 0, FAKE, FAKE, None) == coat.COAT_EINVAL      # group not a power of two
+    assert q(FAKE, 100, 8, 0, FAKE, FAKE, None) == coat.COAT_EINVAL       # group below 16
+    assert q(FAKE, 100, 0, 0x100, FAKE, FAKE, None) == coat.COAT_EINVAL   # no flags on activations
+    assert q(FAKE, -1, 0, 0, FAKE, FAKE, None) == coat.COAT_EINVAL
+    assert q(None, 100, 0, 0, FAKE, FAKE, None) == coat.COAT_EINVAL
+    assert q(FAKE + 2, 100, 128, 1, FAKE, FAKE, None) == coat.COAT_EALIGN
+    assert q(FAKE, 100, 128, 1, FAKE + 8, FAKE, None) == coat.COAT_EALIGN
+    assert q(FAKE, 100, 128, 1, FAKE, FAKE + 2, None) == coat.COAT_EALIGN
+    assert q(None, 0, 0, 0, None, None, None) == coat.COAT_OK
+    assert d(FAKE, FAKE, 100, 2048, 0, FAKE, None) == coat.COAT_EINVAL
+    assert d(FAKE, FAKE, 100, 0, 2, FAKE, None) == coat.COAT_EINVAL
+    assert d(FAKE, FAKE, 100, 0, 0, FAKE + 4, None) == coat.COAT_EALIGN
+    assert d(FAKE, None, 100, 0, 0, FAKE, None) == coat.COAT_EINVAL
 
 
 def test_multi_argument_checks():
