@@ -1083,7 +1083,9 @@ __device__ __forceinline__ double table_dequant_fma(uint32_t w, int i, const uin
 // One wavefront tile of the step: elements [tile*1024, tile*1024 + 1024) of t,
 // inputs in `in`. FULL: every element lies in the tensor and the group work is
 // split over lane pairs (group >= 32), so no lane needs a bounds check.
-template <int FM, int FV, bool FULL, bool TAB>
+// LG: log2 of the group size when fixed at compile time (0: c.lg2_group), so
+// that the lane-group reductions unroll into straight DPP sequences.
+template <int FM, int FV, bool FULL, bool TAB, int LG>
 __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
                                           const ConstTables& ct, WaveLds& wl, TileIn& in) {
     static_assert(!TAB || FULL, "tables only for whole tiles");
@@ -1092,11 +1094,12 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
     const int64_t rem = t.n - e0;
     const int nvalid = FULL ? kLaneElems : (rem <= 0 ? 0 : (rem >= kLaneElems ? kLaneElems : (int)rem));
-    const int lpg = 1 << (c.lg2_group - 4);  // lanes per group
-    const int64_t gidx = e0 >> c.lg2_group;
+    const int lg = LG ? LG : c.lg2_group;
+    const int lpg = 1 << (lg - 4);  // lanes per group
+    const int64_t gidx = e0 >> lg;
     // The lane's group holds elements (possibly not in this lane): its state is
     // stored even by lanes past the end, which take part in the pair's work.
-    const bool gvalid = FULL || (gidx << c.lg2_group) < t.n;
+    const bool gvalid = FULL || (gidx << lg) < t.n;
     const bool pair = FULL || lpg >= 2;      // per-group work split over a lane pair
     // Opaque to the optimizer, so that the per-lane choices between the two
     // formats' constants are made in each tile rather than held in registers
@@ -1378,7 +1381,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) 
             for (int64_t tile = wave_id(); tile < full; tile += nw) {
                 TileIn in;
                 load_full_tile(t, tile, c.lg2_group, in);
-                step_tile<FM, FV, true, TAB>(t, tile, c, ct, wl, in);
+                step_tile<FM, FV, true, TAB, 0>(t, tile, c, ct, wl, in);
             }
         }
         first = full;
@@ -1391,7 +1394,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) 
         for (int64_t tile = first + wave_id(); tile < last; tile += nw) {
             TileIn in;
             load_tile(t, tile, c.lg2_group, in);
-            step_tile<FM, FV, false, false>(t, tile, c, ct, wl, in);
+            step_tile<FM, FV, false, false, 0>(t, tile, c, ct, wl, in);
         }
     }
 }
@@ -1401,7 +1404,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) 
 // workspace. Each wavefront strides over the global full-tile index space,
 // walking the prefix forward to find the tensor of its tile; then the partial
 // tiles take the general path. Phases and TAB as for the single kernel.
-template <int FM, int FV, bool TAB>
+template <int FM, int FV, bool TAB, int LG>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) void step_multi_kernel(
     const TensorRef* __restrict__ ts, const int64_t* __restrict__ full_begin, const int32_t* __restrict__ partial,
     int count, int n_partial, StepConsts c, int phases) {
@@ -1409,23 +1412,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) 
     __shared__ WaveLds wls[kWavesPerBlock];
     WaveLds& wl = wls[threadIdx.x / kWave];
     fill_tables<FM, FV>(ct, c.b1, c.b2);
+    const int lg = LG ? LG : c.lg2_group;
     const int64_t full = full_begin[count];
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     if (phases & kPhaseFull) {
         int cur = 0;
-        if (c.lg2_group >= 5) {
+        if (lg >= 5) {
             for (int64_t tile = wave_id(); tile < full; tile += nw) {
                 while (tile >= full_begin[cur + 1]) ++cur;
                 TileIn in;
-                load_full_tile(ts[cur], tile - full_begin[cur], c.lg2_group, in);
-                step_tile<FM, FV, true, TAB>(ts[cur], tile - full_begin[cur], c, ct, wl, in);
+                load_full_tile(ts[cur], tile - full_begin[cur], lg, in);
+                step_tile<FM, FV, true, TAB, LG>(ts[cur], tile - full_begin[cur], c, ct, wl, in);
             }
         } else if constexpr (!TAB) {
             for (int64_t tile = wave_id(); tile < full; tile += nw) {
                 while (tile >= full_begin[cur + 1]) ++cur;
                 TileIn in;
-                load_tile(ts[cur], tile - full_begin[cur], c.lg2_group, in);
-                step_tile<FM, FV, false, false>(ts[cur], tile - full_begin[cur], c, ct, wl, in);
+                load_tile(ts[cur], tile - full_begin[cur], lg, in);
+                step_tile<FM, FV, false, false, LG>(ts[cur], tile - full_begin[cur], c, ct, wl, in);
             }
         }
     }
@@ -1435,8 +1439,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) 
                 const TensorRef& t = ts[partial[i]];
                 const int64_t tile = t.n / kTile;
                 TileIn in;
-                load_tile(t, tile, c.lg2_group, in);
-                step_tile<FM, FV, false, false>(t, tile, c, ct, wl, in);
+                load_tile(t, tile, lg, in);
+                step_tile<FM, FV, false, false, LG>(t, tile, c, ct, wl, in);
             }
         }
     }
@@ -1986,20 +1990,36 @@ void launch_single(const TensorRef& t, const StepConsts& c, hipStream_t st) {
                        0, st, t, c, kPhaseFull | kPhasePartial);
 }
 
+// The multi-tensor kernels are specialized on the group size (groups of
+// 128 .. 1024 in the table kernel, 16 .. 64 in the direct one); partial tiles
+// of groups of 128 and more take the direct kernel with the size at run time.
+template <int FM, int FV, bool TAB, int LG>
+void launch_multi_lg(const TensorRef* ts, const int64_t* fb, const int32_t* partial, int count, int n_partial,
+                     int64_t waves, const StepConsts& c, int phases, hipStream_t st) {
+    hipLaunchKernelGGL((step_multi_kernel<FM, FV, TAB, LG>), dim3(grid_for(waves, kStepBlocksPerCU)), dim3(kBlock),
+                       0, st, ts, fb, partial, count, n_partial, c, phases);
+}
+
 template <int FM, int FV>
 void launch_multi(const TensorRef* ts, const int64_t* fb, const int32_t* partial, int count, int n_partial,
                   int64_t tiles, int64_t full, const StepConsts& c, hipStream_t st) {
-    if (c.lg2_group >= 7) {
-        if (full > 0)
-            hipLaunchKernelGGL((step_multi_kernel<FM, FV, true>), dim3(grid_for(full, kStepBlocksPerCU)),
-                               dim3(kBlock), 0, st, ts, fb, partial, count, n_partial, c, kPhaseFull);
-        if (n_partial > 0)
-            hipLaunchKernelGGL((step_multi_kernel<FM, FV, false>), dim3(grid_for(n_partial, kStepBlocksPerCU)),
-                               dim3(kBlock), 0, st, ts, fb, partial, count, n_partial, c, kPhasePartial);
-        return;
+    const int both = kPhaseFull | kPhasePartial;
+    switch (c.lg2_group) {
+        case 4: launch_multi_lg<FM, FV, false, 4>(ts, fb, partial, count, n_partial, tiles, c, both, st); return;
+        case 5: launch_multi_lg<FM, FV, false, 5>(ts, fb, partial, count, n_partial, tiles, c, both, st); return;
+        case 6: launch_multi_lg<FM, FV, false, 6>(ts, fb, partial, count, n_partial, tiles, c, both, st); return;
+        default: break;
     }
-    hipLaunchKernelGGL((step_multi_kernel<FM, FV, false>), dim3(grid_for(tiles, kStepBlocksPerCU)), dim3(kBlock),
-                       0, st, ts, fb, partial, count, n_partial, c, kPhaseFull | kPhasePartial);
+    if (full > 0) {
+        switch (c.lg2_group) {
+            case 7: launch_multi_lg<FM, FV, true, 7>(ts, fb, partial, count, n_partial, full, c, kPhaseFull, st); break;
+            case 8: launch_multi_lg<FM, FV, true, 8>(ts, fb, partial, count, n_partial, full, c, kPhaseFull, st); break;
+            case 9: launch_multi_lg<FM, FV, true, 9>(ts, fb, partial, count, n_partial, full, c, kPhaseFull, st); break;
+            default: launch_multi_lg<FM, FV, true, 10>(ts, fb, partial, count, n_partial, full, c, kPhaseFull, st); break;
+        }
+    }
+    if (n_partial > 0)
+        launch_multi_lg<FM, FV, false, 0>(ts, fb, partial, count, n_partial, n_partial, c, kPhasePartial, st);
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
