@@ -166,10 +166,20 @@ constexpr int kCoefExp2 = 0;          // offset of the exp2 coefficients
 constexpr int kCoefLog2 = kExp2N;     // offset of the log2 coefficients
 constexpr int kCoefN = kExp2N + kLog2N;
 
+// a * b + c as the three-address v_fma_f64. With the coefficient (held in a
+// register) as the addend, the compiler otherwise picks the accumulating
+// v_fmac_f64 and copies the coefficient into the accumulator first, one extra
+// move per Horner step.
+__device__ __forceinline__ double fma3(double a, double b, double c) {
+    double r;
+    asm("v_fma_f64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(c));
+    return r;
+}
+
 __device__ __forceinline__ double exp2_poly10(double f) {
     double p = kExp2C[0];
 #pragma unroll
-    for (int i = 1; i < kExp2N; ++i) p = __builtin_fma(p, f, kExp2C[i]);
+    for (int i = 1; i < kExp2N; ++i) p = fma3(p, f, kExp2C[i]);
     return p;
 }
 __device__ __forceinline__ double exp2_poly10(double f, CoefPtr cf) {
@@ -255,7 +265,7 @@ __device__ __forceinline__ double log2_dd_impl(double x, double& lo, C c) {
     const double w = u * u;
     double p = c[0];
 #pragma unroll
-    for (int i = 1; i < kLog2N; ++i) p = __builtin_fma(p, w, c[i]);
+    for (int i = 1; i < kLog2N; ++i) p = fma3(p, w, c[i]);
     const double ed = (double)e;
     const double hi = __builtin_fma(u, p, ed);
     lo = __builtin_fma(u, p, ed - hi);  // ed - hi is exact (|u p| <= 1/2)
@@ -414,24 +424,55 @@ struct alignas(16) LqEntry {
     double lq;
     double b;
 };
-struct ConstTables {
+// Tables of the direct path and of the codec kernels.
+struct DirectTables {
     LqEntry lqb[2][256];
     double lqm[2][128];
     double coef[kCoefN];
+};
+// Tables of the table path: lq without the sign and decay (only its rare
+// exact paths dequantize code by code), the per-code table offsets and the
+// builder lanes' jobs.
+struct TabTables {
+    double lq[2][128];
+    double lqm[2][128];
+    double coef[kCoefN];
     uint32_t lut[2][256];  // per-group table offsets of each code (see GroupTable)
-    double lsi[16][2];     // log2(i), i = 0..15, as hi + lo
+    LaneJob lj[8];         // per builder lane (moment * 4 + lane in quad)
+};
+// Set-up scratch of the table path, in LDS that the waves use later.
+struct TabScratch {
     TableJobs jobs[2];     // how the lanes of a group build each moment's table
-    LaneJob lj[8];         // the same per builder lane (moment * 4 + lane in quad)
 };
 
 // The coefficient copy, through a pointer the optimizer cannot see through
 // (so that per-tile code reloads the coefficients from LDS instead of hoisting
 // them into registers across the tile loop).
-__device__ __forceinline__ CoefPtr coef_ptr(const ConstTables& ct) {
-    uint32_t a = (uint32_t)(uintptr_t)(CoefPtr)ct.coef;
+__device__ __forceinline__ CoefPtr coef_ptr(const double* coef) {
+    uint32_t a = (uint32_t)(uintptr_t)(CoefPtr)coef;
     asm volatile("" : "+v"(a));
     return (CoefPtr)(uintptr_t)a;
 }
+
+// The dequantization constants of a code, with the sign and decay folded into
+// tb (direct path: from the 256-entry table) ...
+struct LqSigned {
+    const LqEntry* t;
+    __device__ double get(uint32_t c, double& tb) const {
+        const LqEntry e = t[c];
+        tb = e.b;
+        return e.lq;
+    }
+};
+// ... or with tb formed from the code's sign (table path).
+struct LqSplit {
+    const double* lq;
+    double b;
+    __device__ double get(uint32_t c, double& tb) const {
+        tb = (c & 0x80u) ? -b : b;
+        return lq[c & 0x7Fu];
+    }
+};
 
 template <int F>
 __device__ double lq_entry(int c) {
@@ -465,17 +506,23 @@ __device__ double lqm_entry(int c) {
 // exponent field and i its integer significand (the mantissa field, plus
 // 2^MB when e > 0), so a group's dequantized, decay-scaled moment
 // b sign(q) (|q| s)^(1/k) = b 2^(a + r (max(e,1) - BIAS - MB - log2 fpmax)) * sign i^r
-// is the product of two table entries: TE[e] (32 slots, times b) and
-// TS[j], j = i + NEG * sign (32 slots). TE[31] holds NaN (E4M3: its NaN
-// code) or Inf (E5M2: e = 31); TS[31] holds NaN for E5M2's NaN codes.
+// is the product of two table entries: TE[e] (times b) and TS[j],
+// j = i + NEG * sign. Layout (entries of one table):
+//   E4M3: TE[0..15], NaN at 16 (its NaN code); TS[0..31] at 17..48;
+//   E5M2: TE[0..30], Inf at 31 (e = 31); TS[0..15] at 32..47, NaN at 48
+//         (its NaN codes);
+//   both: the powers (2^r)^0..3 at 49..52, a trash slot at 53.
+constexpr int kGroupTableN = 54;
+constexpr int kPowBase = 49;
+constexpr int kTrash = 53;
 struct GroupTable {
-    // TE = v[0..31], TS = v[32..63], the powers (2^r)^0..3 at v[64..67], a
-    // trash slot v[68]; the odd size spreads the groups over the LDS banks
-    double v[69];
+    double v[kGroupTableN];
 };
-constexpr int kTsBase = 32;
-constexpr int kPowBase = 64;
-constexpr int kTrash = 68;
+template <int F>
+constexpr int ts_base() { return F == COAT_FMT_E4M3 ? 17 : 32; }
+template <int F>
+constexpr int te_special() { return F == COAT_FMT_E4M3 ? 16 : 31; }
+constexpr int kE5TsNan = 16;
 template <int F>
 __device__ uint32_t lut_entry(int code) {
     using T = Fmt<F>;
@@ -483,11 +530,11 @@ __device__ uint32_t lut_entry(int code) {
     const int mag = code & 0x7F, e = mag >> T::MB, m = mag & ((1 << T::MB) - 1);
     int te = e, ts = (e ? (m | (1 << T::MB)) : m) + ((code & 0x80) ? NEG : 0);
     if (T::is_nan(mag)) {
-        te = 31;
-        if (F == COAT_FMT_E5M2) ts = 31;
+        te = te_special<F>();
+        if (F == COAT_FMT_E5M2) ts = kE5TsNan;
     }
     const uint32_t te_off = (uint32_t)(te * 8);
-    const uint32_t ts_off = (uint32_t)((kTsBase + ts) * 8);
+    const uint32_t ts_off = (uint32_t)((ts_base<F>() + ts) * 8);
     return te_off | (ts_off << 16);
 }
 
@@ -505,14 +552,14 @@ __device__ void table_jobs(TableJobs& j, int tid) {
     using T = Fmt<F>;
     constexpr bool E4 = F == COAT_FMT_E4M3;
     constexpr int NTS = E4 ? 8 : 4;
-    constexpr int TRASH = E4 ? 16 : kTsBase + 16;  // E4M3 has no TE[16..30]; E5M2 no TS[16..30]
+    constexpr int TSB = ts_base<F>();
     if (tid < 12) {
         ExpJob& e = j.e[tid];
         if (tid < NTS) {
             const int ts[8] = {2, 3, 5, 7, 9, 11, 13, 15};
             const int i = ts[tid];
             e.xh = log2_full_dd((double)i, e.xl);
-            e.slot = kTsBase + i;
+            e.slot = TSB + i;
             e.te = 0;
         } else {
             const int a = 4 * (tid - NTS);
@@ -526,13 +573,13 @@ __device__ void table_jobs(TableJobs& j, int tid) {
         }
     } else if (tid < 12 + 28) {
         const int q = tid - 12;
-        ProdJob pj{0, 0, (uint8_t)TRASH, 0};
+        ProdJob pj{0, 0, (uint8_t)kTrash, 0};
         // TS products first, then the TE chains
         const int ts_src[6] = {2, 3, 2, 5, 3, 7}, ts_pow[6] = {1, 1, 2, 1, 2, 1}, ts_dst[6] = {4, 6, 8, 10, 12, 14};
         const int nts = E4 ? 6 : 2;
         const int nte = (E4 ? 4 : 8) * 3;
         if (q < nts) {
-            pj = ProdJob{(uint8_t)(kTsBase + ts_src[q]), (uint8_t)ts_pow[q], (uint8_t)(kTsBase + ts_dst[q]), 1};
+            pj = ProdJob{(uint8_t)(TSB + ts_src[q]), (uint8_t)ts_pow[q], (uint8_t)(TSB + ts_dst[q]), 1};
         } else if (q < nts + nte) {
             const int r = q - nts, a = 4 * (r / 3), jj = 1 + r % 3;
             pj = ProdJob{(uint8_t)a, (uint8_t)(a == 0 ? jj - 1 : jj), (uint8_t)(a + jj), 0};
@@ -544,7 +591,7 @@ __device__ void table_jobs(TableJobs& j, int tid) {
 // Filled by the block's 256 threads: thread i covers moment i >> 7, code i & 127
 // and its negative.
 template <int FM, int FV>
-__device__ __forceinline__ void fill_tables(ConstTables& ct, double bm, double bv) {
+__device__ __forceinline__ void fill_direct_tables(DirectTables& ct, double bm, double bv) {
     const int f = threadIdx.x >> 7, c = threadIdx.x & 127;
     const double lq = f ? lq_entry<FV>(c) : lq_entry<FM>(c);
     const double b = f ? bv : bm;
@@ -553,22 +600,28 @@ __device__ __forceinline__ void fill_tables(ConstTables& ct, double bm, double b
     ct.lqm[f][c] = f ? lqm_entry<FV>(c) : lqm_entry<FM>(c);
     if (threadIdx.x < kCoefN)
         ct.coef[threadIdx.x] = threadIdx.x < kExp2N ? kExp2C[threadIdx.x] : kLog2C[threadIdx.x - kExp2N];
+    __syncthreads();
+}
+
+// The same for the table path; `scratch` (LDS the waves use later) holds the
+// job lists while the per-lane jobs are derived from them.
+template <int FM, int FV>
+__device__ __forceinline__ void fill_tab_tables(TabTables& ct, TabScratch& scratch, double bm, double bv) {
+    const int f = threadIdx.x >> 7, c = threadIdx.x & 127;
+    ct.lq[f][c] = f ? lq_entry<FV>(c) : lq_entry<FM>(c);
+    ct.lqm[f][c] = f ? lqm_entry<FV>(c) : lqm_entry<FM>(c);
+    if (threadIdx.x < kCoefN)
+        ct.coef[threadIdx.x] = threadIdx.x < kExp2N ? kExp2C[threadIdx.x] : kLog2C[threadIdx.x - kExp2N];
     ct.lut[f][c] = f ? lut_entry<FV>(c) : lut_entry<FM>(c);
     ct.lut[f][c | 128] = f ? lut_entry<FV>(c | 128) : lut_entry<FM>(c | 128);
-    if (threadIdx.x < 64) table_jobs<FM>(ct.jobs[0], threadIdx.x);
-    else if (threadIdx.x < 128) table_jobs<FV>(ct.jobs[1], threadIdx.x - 64);
-    if (threadIdx.x < 16) {
-        double lo = 0.0;
-        const double hi = threadIdx.x > 0 ? log2_full_dd((double)threadIdx.x, lo) : 0.0;
-        ct.lsi[threadIdx.x][0] = hi;
-        ct.lsi[threadIdx.x][1] = lo;
-    }
+    if (threadIdx.x < 64) table_jobs<FM>(scratch.jobs[0], threadIdx.x);
+    else if (threadIdx.x < 128) table_jobs<FV>(scratch.jobs[1], threadIdx.x - 64);
     __syncthreads();
     if (threadIdx.x < 8) {
         const int mu = threadIdx.x >> 2, t = threadIdx.x & 3;
         const bool e4 = (mu ? FV : FM) == COAT_FMT_E4M3;
         const uint32_t NEG = e4 ? 16 : 8;
-        const TableJobs& J = ct.jobs[mu];
+        const TableJobs& J = scratch.jobs[mu];
         LaneJob& L = ct.lj[threadIdx.x];
         for (int q = 0; q < 3; ++q) {
             const ExpJob& e = J.e[3 * t + q];
@@ -589,6 +642,7 @@ __device__ __forceinline__ void fill_tables(ConstTables& ct, double bm, double b
     }
     __syncthreads();
 }
+
 
 // ------------------------------------------------------------------ group state
 
@@ -807,11 +861,10 @@ static_assert(sizeof(TensorRef) == sizeof(coat_tensor), "descriptor layout");
 // Dequantize byte i of code word w: returns the magnitude
 // 2^(LQ[c] r + a + a_lo) and sets tb to the code's table factor (+/- b), so
 // that the signed value times b is tb * magnitude.
-__device__ __forceinline__ double dequant_mag(uint32_t w, int i, const OldGroup& og, const LqEntry* t,
-                                              double& tb) {
-    const LqEntry e = t[(w >> (8 * i)) & 0xFFu];
-    tb = e.b;
-    const double u = __builtin_fma(e.lq, og.r, og.a);
+template <typename L>
+__device__ __forceinline__ double dequant_mag(uint32_t w, int i, const OldGroup& og, const L& src, double& tb) {
+    const double lq = src.get((w >> (8 * i)) & 0xFFu, tb);
+    const double u = __builtin_fma(lq, og.r, og.a);
     const double n = __builtin_rint(u);
     return __builtin_amdgcn_ldexp(exp2_poly10((u - n) + og.a_lo), cvt_i32_sat(n));
 }
@@ -829,12 +882,17 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t word, int half) {
 // Per-wave LDS area holding, after the element pass, the inputs that only the
 // exact requantization needs (raw codes and grads, dequantization constants),
 // so that no registers are held for them through the requantization.
-struct Park {
+struct ParkDirect {
     uint32_t gw[8][kWave];
     uint32_t mq[4][kWave];
     uint32_t vq[4][kWave];
-    double og[6][kWave];  // direct path: m: a, a_lo, r; v: a, a_lo, r
-    double s[2][kWave];   // table path: the stored scales as loaded (TileIn s0, s1)
+    double og[6][kWave];  // m: a, a_lo, r; v: a, a_lo, r
+};
+struct ParkTab {
+    uint32_t gw[8][kWave];
+    uint32_t mq[4][kWave];
+    uint32_t vq[4][kWave];
+    double s[2][kWave];   // the stored scales as loaded (TileIn s0, s1)
     float k[2][kWave];    // and exponents (k0, k1), from which the rare paths recompute them
 };
 
@@ -845,10 +903,10 @@ struct Park {
 // dequantization constants), then rounded with the fp64 threshold (or from scratch for
 // groups outside the fp32 path's range). Loops until no lane has a flagged
 // element.
-template <int F>
+template <int F, typename PK, typename L>
 __device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&codes)[4],
-                                               const uint32_t (*old)[kWave], const Park& pk, const OldGroup& og,
-                                               const NewGroup& ng, const LqEntry* lq, const double* lqm,
+                                               const uint32_t (*old)[kWave], const PK& pk, const OldGroup& og,
+                                               const NewGroup& ng, const L& lq, const double* lqm,
                                                const FmtRT& F_, double cb, bool square, CoefPtr cf) {
     const int lane = threadIdx.x & (kWave - 1);
     while (__any((amb[0] | amb[1] | amb[2] | amb[3]) != 0u)) {
@@ -984,10 +1042,27 @@ __device__ __forceinline__ void load_full_tile(const TensorRef& t, int64_t tile,
     in.k1 = 1.0f;
 }
 
-// Per-wave LDS: the group tables during the element pass, then the park area.
-union WaveLds {
+// Per-wave LDS of the table path: the group tables during the element pass,
+// then the park area; of the direct path: the park area.
+union WaveLdsTab {
     GroupTable tbl[16];
-    Park pk;
+    ParkTab pk;
+    TabScratch setup;  // wave 0's, during the block's set-up only
+};
+struct WaveLdsDirect {
+    ParkDirect pk;
+};
+template <bool TAB>
+struct StepLds;
+template <>
+struct StepLds<true> {
+    using Tables = TabTables;
+    using Wave = WaveLdsTab;
+};
+template <>
+struct StepLds<false> {
+    using Tables = DirectTables;
+    using Wave = WaveLdsDirect;
 };
 
 // 2^(h + l) for a double-double exponent with |l| small.
@@ -1019,7 +1094,7 @@ __device__ __forceinline__ void fma_dd(double ah, double al, double rh, double r
 // each taking its LaneJob. Every entry is a correctly rounded 2^(A + r x)
 // with a double-double exponent, or a product of at most three such values.
 template <int FM, int FV>
-__device__ __forceinline__ void build_tables(WaveLds& wl, const ConstTables& ct, const OldGroup& om,
+__device__ __forceinline__ void build_tables(WaveLdsTab& wl, const TabTables& ct, const OldGroup& om,
                                              const OldGroup& ov, int lpg) {
     // opaque, so that the lane's job parameters are derived in each tile
     // instead of being hoisted out of the tile loop into registers
@@ -1028,6 +1103,8 @@ __device__ __forceinline__ void build_tables(WaveLds& wl, const ConstTables& ct,
     const int l = lane & (lpg - 1);
     if (l >= 8) return;
     const int mu = l >> 2, t = l & 3;
+    const bool e4 = (mu ? FV : FM) == COAT_FMT_E4M3;
+    const int tsb = e4 ? ts_base<COAT_FMT_E4M3>() : ts_base<COAT_FMT_E5M2>();
     char* gb = reinterpret_cast<char*>(&wl.tbl[(lane / lpg) * 2 + mu]);
     auto at = [&](uint32_t off) -> double& { return *reinterpret_cast<double*>(gb + off); };
     const double a = mu ? ov.a : om.a, a_lo = mu ? ov.a_lo : om.a_lo;
@@ -1043,7 +1120,7 @@ __device__ __forceinline__ void build_tables(WaveLds& wl, const ConstTables& ct,
     }
     asm volatile("" ::: "memory");
     if (t == 0) {
-        const double P = at(8u * (kTsBase + 2));
+        const double P = at(8u * (tsb + 2));
         at(8u * kPowBase) = 1.0;
         at(8u * (kPowBase + 1)) = P;
         at(8u * (kPowBase + 2)) = P * P;
@@ -1057,15 +1134,18 @@ __device__ __forceinline__ void build_tables(WaveLds& wl, const ConstTables& ct,
         at(J.ndst[q]) = -v;
     }
     if (t == 3) {
-        const bool e4 = (mu ? FV : FM) == COAT_FMT_E4M3;
         const int NEG = e4 ? 16 : 8;
         double* g = reinterpret_cast<double*>(gb);
-        g[kTsBase] = 0.0;
-        g[kTsBase + NEG] = -0.0;
-        g[kTsBase + 1] = 1.0;
-        g[kTsBase + 1 + NEG] = -1.0;
-        g[31] = e4 ? __builtin_nan("") : __builtin_inf();
-        if (!e4) g[kTsBase + 31] = __builtin_nan("");
+        g[tsb] = 0.0;
+        g[tsb + NEG] = -0.0;
+        g[tsb + 1] = 1.0;
+        g[tsb + 1 + NEG] = -1.0;
+        if (e4) {
+            g[te_special<COAT_FMT_E4M3>()] = __builtin_nan("");
+        } else {
+            g[te_special<COAT_FMT_E5M2>()] = __builtin_inf();
+            g[tsb + kE5TsNan] = __builtin_nan("");
+        }
     }
     asm volatile("" ::: "memory");
 }
@@ -1085,11 +1165,15 @@ __device__ __forceinline__ double table_dequant_fma(uint32_t w, int i, const uin
 // split over lane pairs (group >= 32), so no lane needs a bounds check.
 // LG: log2 of the group size when fixed at compile time (0: c.lg2_group), so
 // that the lane-group reductions unroll into straight DPP sequences.
+__device__ __forceinline__ LqSigned lq_source(const DirectTables& ct, int f, double) { return LqSigned{ct.lqb[f]}; }
+__device__ __forceinline__ LqSplit lq_source(const TabTables& ct, int f, double b) { return LqSplit{ct.lq[f], b}; }
+
 template <int FM, int FV, bool FULL, bool TAB, int LG>
 __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
-                                          const ConstTables& ct, WaveLds& wl, TileIn& in) {
+                                          const typename StepLds<TAB>::Tables& ct,
+                                          typename StepLds<TAB>::Wave& wl, TileIn& in) {
     static_assert(!TAB || FULL, "tables only for whole tiles");
-    Park& pk = wl.pk;
+    auto& pk = wl.pk;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
     const int64_t rem = t.n - e0;
@@ -1107,7 +1191,7 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     int odd_bit = lane & 1;
     asm volatile("" : "+v"(odd_bit));
     const bool odd = odd_bit != 0;
-    const CoefPtr cf = coef_ptr(ct);
+    const CoefPtr cf = coef_ptr(ct.coef);
     const FmtRT fm = fmt_rt<FM>(), fv = fmt_rt<FV>();
 
     gfloat* P = gp(t.p);
@@ -1145,8 +1229,8 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     groups_of(in.s0, in.k0, in.s1, in.k1, om, ov);
 
     // ---- per element: dequantize, moments, statistics, AdamW update
-    const LqEntry* lq_m = ct.lqb[0];
-    const LqEntry* lq_v = ct.lqb[1];
+    const auto lq_m = lq_source(ct, 0, c.b1);
+    const auto lq_v = lq_source(ct, 1, c.b2);
     float xm[16], xv[16];
     double amax_m = 0.0, amin_m = __builtin_inf(), amax_v = 0.0, amin_v = __builtin_inf();
     // sum of xm * xv: not finite if any moment is infinite or NaN (or beyond fp32)
@@ -1366,12 +1450,13 @@ constexpr int kPhasePartial = 2;  // last tiles that end inside their tensor
 // per-group tables, and nothing else; otherwise the tiles of `phases` on the
 // direct path (group 16: every tile on the general path).
 template <int FM, int FV, bool TAB>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) void step_single_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAB ? 4 : 3, TAB ? 4 : 3))) void step_single_kernel(
     TensorRef t, StepConsts c, int phases) {
-    __shared__ ConstTables ct;
-    __shared__ WaveLds wls[kWavesPerBlock];
-    WaveLds& wl = wls[threadIdx.x / kWave];
-    fill_tables<FM, FV>(ct, c.b1, c.b2);
+    __shared__ typename StepLds<TAB>::Tables ct;
+    __shared__ typename StepLds<TAB>::Wave wls[kWavesPerBlock];
+    auto& wl = wls[threadIdx.x / kWave];
+    if constexpr (TAB) fill_tab_tables<FM, FV>(ct, wls[0].setup, c.b1, c.b2);
+    else fill_direct_tables<FM, FV>(ct, c.b1, c.b2);
     const int64_t full = t.n / kTile;
     const int64_t tiles = (t.n + kTile - 1) / kTile;
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
@@ -1405,13 +1490,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) 
 // walking the prefix forward to find the tensor of its tile; then the partial
 // tiles take the general path. Phases and TAB as for the single kernel.
 template <int FM, int FV, bool TAB, int LG>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3, 3))) void step_multi_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAB ? 4 : 3, TAB ? 4 : 3))) void step_multi_kernel(
     const TensorRef* __restrict__ ts, const int64_t* __restrict__ full_begin, const int32_t* __restrict__ partial,
     int count, int n_partial, StepConsts c, int phases) {
-    __shared__ ConstTables ct;
-    __shared__ WaveLds wls[kWavesPerBlock];
-    WaveLds& wl = wls[threadIdx.x / kWave];
-    fill_tables<FM, FV>(ct, c.b1, c.b2);
+    __shared__ typename StepLds<TAB>::Tables ct;
+    __shared__ typename StepLds<TAB>::Wave wls[kWavesPerBlock];
+    auto& wl = wls[threadIdx.x / kWave];
+    if constexpr (TAB) fill_tab_tables<FM, FV>(ct, wls[0].setup, c.b1, c.b2);
+    else fill_direct_tables<FM, FV>(ct, c.b1, c.b2);
     const int lg = LG ? LG : c.lg2_group;
     const int64_t full = full_begin[count];
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
@@ -1453,8 +1539,8 @@ template <int F>
 __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restrict__ x, int64_t n,
                                                           int lg2_group, int expand, uint8_t* q,
                                                           double* s, float* k) {
-    __shared__ ConstTables ct;
-    fill_tables<F, F>(ct, 1.0, 1.0);
+    __shared__ DirectTables ct;
+    fill_direct_tables<F, F>(ct, 1.0, 1.0);
     const int64_t tiles = (n + kTile - 1) / kTile;
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1490,7 +1576,7 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
         amin = group_min(amin, lpg);
         const bool poison = group_or(bad ? 1u : 0u, lpg) != 0u;
         double la_lo, lb_lo;
-        const CoefPtr cf = coef_ptr(ct);
+        const CoefPtr cf = coef_ptr(ct.coef);
         const double la = log2_stat(amax, la_lo), lb = log2_stat(amin, lb_lo);
         const NewGroup ng = new_group(amax, amin, la, la_lo, lb, lb_lo, poison, expand, fr);
         uint32_t cw[4], amb[4];
@@ -1552,8 +1638,8 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __res
                                                             const double* __restrict__ s,
                                                             const float* __restrict__ k, int64_t n,
                                                             int lg2_group, float* __restrict__ x) {
-    __shared__ ConstTables ct;
-    fill_tables<F, F>(ct, 1.0, 1.0);
+    __shared__ DirectTables ct;
+    fill_direct_tables<F, F>(ct, 1.0, 1.0);
     const int64_t tiles = (n + kTile - 1) / kTile;
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1573,7 +1659,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __res
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 double tb;
-                const double mag = dequant_mag(w[i >> 2], i & 3, og, ct.lqb[0], tb);
+                const double mag = dequant_mag(w[i >> 2], i & 3, og, LqSigned{ct.lqb[0]}, tb);
                 out[i] = (float)(tb * mag);
             }
 #pragma unroll
@@ -1584,7 +1670,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __res
             for (int i = 0; i < 16; ++i)
                 if (i < nvalid) {
                     double tb;
-                    const double mag = dequant_mag(Q[e0 + i], 0, og, ct.lqb[0], tb);
+                    const double mag = dequant_mag(Q[e0 + i], 0, og, LqSigned{ct.lqb[0]}, tb);
                     X[e0 + i] = (float)(tb * mag);
                 }
         }
