@@ -1017,29 +1017,34 @@ __device__ __forceinline__ void load_tile(const TensorRef& t, int64_t tile, int 
 
 // Loads of a tile that lies wholly inside its tensor, for group sizes whose
 // per-group work is split over lane pairs (even lane m, odd lane v).
+// Issued in the order the tile consumes them (vmcnt retires in order): the
+// stored scales first (the group constants and tables need only them), then
+// the codes, grads and master weights, all before any use.
 __device__ __forceinline__ void load_full_tile(const TensorRef& t, int64_t tile, int lg2_group, TileIn& in) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
     const int64_t gidx = e0 >> lg2_group;
     const bool odd = (lane & 1) != 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const f32x4 v = reinterpret_cast<const gf32x4*>(gp(t.p) + e0)[i];
-        in.p[4 * i] = v.x; in.p[4 * i + 1] = v.y; in.p[4 * i + 2] = v.z; in.p[4 * i + 3] = v.w;
-    }
+    in.s0 = gp(odd ? uniform_ptr(t.vs) : uniform_ptr(t.ms))[gidx];
+    in.k0 = gp(odd ? uniform_ptr(t.vk) : uniform_ptr(t.mk))[gidx];
+    in.s1 = 0.0;
+    in.k1 = 1.0f;
+    const u32x4 a = *reinterpret_cast<const gu32x4*>(gp(t.mq) + e0);
+    in.mq[0] = a.x; in.mq[1] = a.y; in.mq[2] = a.z; in.mq[3] = a.w;
+    const u32x4 b = *reinterpret_cast<const gu32x4*>(gp(t.vq) + e0);
+    in.vq[0] = b.x; in.vq[1] = b.y; in.vq[2] = b.z; in.vq[3] = b.w;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const u32x4 v = reinterpret_cast<const gu32x4*>(gp(t.g) + e0)[i];
         in.gw[4 * i] = v.x; in.gw[4 * i + 1] = v.y; in.gw[4 * i + 2] = v.z; in.gw[4 * i + 3] = v.w;
     }
-    const u32x4 a = *reinterpret_cast<const gu32x4*>(gp(t.mq) + e0);
-    in.mq[0] = a.x; in.mq[1] = a.y; in.mq[2] = a.z; in.mq[3] = a.w;
-    const u32x4 b = *reinterpret_cast<const gu32x4*>(gp(t.vq) + e0);
-    in.vq[0] = b.x; in.vq[1] = b.y; in.vq[2] = b.z; in.vq[3] = b.w;
-    in.s0 = gp(odd ? uniform_ptr(t.vs) : uniform_ptr(t.ms))[gidx];
-    in.k0 = gp(odd ? uniform_ptr(t.vk) : uniform_ptr(t.mk))[gidx];
-    in.s1 = 0.0;
-    in.k1 = 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x4 v = reinterpret_cast<const gf32x4*>(gp(t.p) + e0)[i];
+        in.p[4 * i] = v.x; in.p[4 * i + 1] = v.y; in.p[4 * i + 2] = v.z; in.p[4 * i + 3] = v.w;
+    }
+    // every load is issued before any use of what they return
+    asm volatile("" : "+v"(in.s0), "+v"(in.k0) :: "memory");
 }
 
 // Per-wave LDS of the table path: the group tables during the element pass,
@@ -1249,6 +1254,10 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
             xm[i] = (float)m1;
             xv[i] = (float)v1;
             fin = __builtin_fmaf(xm[i], xv[i], fin);
+        }
+        // the master weights last: their loads were issued last
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
             const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(xv[i]), c.ib2, c.eps);
             const float upd = xm[i] * __builtin_amdgcn_rcpf(den);
             p[i] = __builtin_fmaf(-c.ssz, upd, p[i] * c.decay);
