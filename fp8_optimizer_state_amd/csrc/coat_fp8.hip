@@ -732,6 +732,7 @@ __device__ NewGroup new_group(double amax, double amin, double L, double L_lo, d
     const double lo = -1022.0 + F.log2_rf, hi = 1023.0;
     const double kL = (double)k * L;
     if (!(kL >= lo && kL <= hi)) {
+        asm volatile("");  // rare: not to be computed speculatively on the common path
         const double bound = (L < 0.0) ? lo / L : hi / L;
         float kk = (float)bound;
         if (kk > k) kk = k;
@@ -892,8 +893,8 @@ struct ParkTab {
     uint32_t gw[8][kWave];
     uint32_t mq[4][kWave];
     uint32_t vq[4][kWave];
-    double s[2][kWave];   // the stored scales as loaded (TileIn s0, s1)
-    float k[2][kWave];    // and exponents (k0, k1), from which the rare paths recompute them
+    double s[kWave];      // the stored scale and exponent as loaded (the lane's moment, TileIn s0,
+    float k[kWave];       // k0), from which the rare paths recompute the group constants
 };
 
 // Exact decision for the elements whose fast code is flagged in `amb` (one
@@ -1020,11 +1021,15 @@ __device__ __forceinline__ void load_tile(const TensorRef& t, int64_t tile, int 
 // Issued in the order the tile consumes them (vmcnt retires in order): the
 // stored scales first (the group constants and tables need only them), then
 // the codes, grads and master weights, all before any use.
+// QUAD (table path): lanes 4..7 of each 8 load the second moment's scale and
+// exponent, lanes 0..3 the first's (the moment whose table the lane builds);
+// otherwise odd lanes the second's and even lanes the first's.
+template <bool QUAD = false>
 __device__ __forceinline__ void load_full_tile(const TensorRef& t, int64_t tile, int lg2_group, TileIn& in) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
     const int64_t gidx = e0 >> lg2_group;
-    const bool odd = (lane & 1) != 0;
+    const bool odd = ((QUAD ? lane >> 2 : lane) & 1) != 0;
     in.s0 = gp(odd ? uniform_ptr(t.vs) : uniform_ptr(t.ms))[gidx];
     in.k0 = gp(odd ? uniform_ptr(t.vk) : uniform_ptr(t.mk))[gidx];
     in.s1 = 0.0;
@@ -1099,8 +1104,7 @@ __device__ __forceinline__ void fma_dd(double ah, double al, double rh, double r
 // each taking its LaneJob. Every entry is a correctly rounded 2^(A + r x)
 // with a double-double exponent, or a product of at most three such values.
 template <int FM, int FV>
-__device__ __forceinline__ void build_tables(WaveLdsTab& wl, const TabTables& ct, const OldGroup& om,
-                                             const OldGroup& ov, int lpg) {
+__device__ __forceinline__ void build_tables(WaveLdsTab& wl, const TabTables& ct, const OldGroup& og, int lpg) {
     // opaque, so that the lane's job parameters are derived in each tile
     // instead of being hoisted out of the tile loop into registers
     int lane = threadIdx.x & (kWave - 1);
@@ -1112,8 +1116,7 @@ __device__ __forceinline__ void build_tables(WaveLdsTab& wl, const TabTables& ct
     const int tsb = e4 ? ts_base<COAT_FMT_E4M3>() : ts_base<COAT_FMT_E5M2>();
     char* gb = reinterpret_cast<char*>(&wl.tbl[(lane / lpg) * 2 + mu]);
     auto at = [&](uint32_t off) -> double& { return *reinterpret_cast<double*>(gb + off); };
-    const double a = mu ? ov.a : om.a, a_lo = mu ? ov.a_lo : om.a_lo;
-    const double r = mu ? ov.r : om.r, r_lo = mu ? ov.r_lo : om.r_lo;
+    const double a = og.a, a_lo = og.a_lo, r = og.r, r_lo = og.r_lo;
     const LaneJob& J = ct.lj[l];
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
@@ -1221,17 +1224,26 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
             gv = old_group(s1, k1, fv.log2_fpmax, fv.log2_fpmax_lo);
         }
     };
+    // Table path: a lane holds the state of moment (lane >> 2) & 1, the one
+    // whose table it builds; lane i and lane 7 - i of each 8 hold the two.
+    const bool q_odd = ((lane >> 2) & 1) != 0;
+    auto own_group = [&](double s0, float k0) {
+        return old_group(s0, k0, q_odd ? fv.log2_fpmax : fm.log2_fpmax, q_odd ? fv.log2_fpmax_lo : fm.log2_fpmax_lo);
+    };
     // the same from the parked state (rare paths, after the element pass)
     auto parked_groups = [&](OldGroup& gm, OldGroup& gv) {
         if constexpr (TAB) {
-            groups_of(pk.s[0][lane], pk.k[0][lane], pk.s[1][lane], pk.k[1][lane], gm, gv);
+            const OldGroup mine = own_group(pk.s[lane], pk.k[lane]);
+            const OldGroup other{xlane64(mine.a, 4), xlane64(mine.a_lo, 4), xlane64(mine.r, 4), xlane64(mine.r_lo, 4)};
+            gm = q_odd ? other : mine;
+            gv = q_odd ? mine : other;
         } else {
             gm = OldGroup{pk.og[0][lane], pk.og[1][lane], pk.og[2][lane], 0.0};
             gv = OldGroup{pk.og[3][lane], pk.og[4][lane], pk.og[5][lane], 0.0};
         }
     };
     OldGroup om, ov;
-    groups_of(in.s0, in.k0, in.s1, in.k1, om, ov);
+    if constexpr (!TAB) groups_of(in.s0, in.k0, in.s1, in.k1, om, ov);
 
     // ---- per element: dequantize, moments, statistics, AdamW update
     const auto lq_m = lq_source(ct, 0, c.b1);
@@ -1265,7 +1277,7 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     };
     if constexpr (TAB) {
         // groups of 128 and more: per-group tables
-        build_tables<FM, FV>(wl, ct, om, ov, lpg);
+        build_tables<FM, FV>(wl, ct, own_group(in.s0, in.k0), lpg);
         const GroupTable& tm = wl.tbl[(lane / lpg) * 2];
         const GroupTable& tv = wl.tbl[(lane / lpg) * 2 + 1];
         element_pass([&](int i, double cg, double cg2, double& m1, double& v1) {
@@ -1291,8 +1303,8 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
 #pragma unroll
     for (int i = 0; i < 4; ++i) { pk.mq[i][lane] = mq[i]; pk.vq[i][lane] = vq[i]; }
     if constexpr (TAB) {
-        pk.s[0][lane] = in.s0; pk.s[1][lane] = in.s1;
-        pk.k[0][lane] = in.k0; pk.k[1][lane] = in.k1;
+        pk.s[lane] = in.s0;
+        pk.k[lane] = in.k0;
     } else {
         pk.og[0][lane] = om.a; pk.og[1][lane] = om.a_lo; pk.og[2][lane] = om.r;
         pk.og[3][lane] = ov.a; pk.og[4][lane] = ov.a_lo; pk.og[5][lane] = ov.r;
@@ -1474,7 +1486,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAB ? 4 
         if (phases & kPhaseFull) {
             for (int64_t tile = wave_id(); tile < full; tile += nw) {
                 TileIn in;
-                load_full_tile(t, tile, c.lg2_group, in);
+                load_full_tile<TAB>(t, tile, c.lg2_group, in);
                 step_tile<FM, FV, true, TAB, 0>(t, tile, c, ct, wl, in);
             }
         }
@@ -1516,7 +1528,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAB ? 4 
             for (int64_t tile = wave_id(); tile < full; tile += nw) {
                 while (tile >= full_begin[cur + 1]) ++cur;
                 TileIn in;
-                load_full_tile(ts[cur], tile - full_begin[cur], lg, in);
+                load_full_tile<TAB>(ts[cur], tile - full_begin[cur], lg, in);
                 step_tile<FM, FV, true, TAB, LG>(ts[cur], tile - full_begin[cur], c, ct, wl, in);
             }
         } else if constexpr (!TAB) {
