@@ -756,11 +756,13 @@ __device__ NewGroup new_group(double amax, double amin, double L, double L_lo, d
 __device__ __forceinline__ OldGroup swap_pair(const OldGroup& g) {
     return OldGroup{dpp64<kDppXor1>(g.a), dpp64<kDppXor1>(g.a_lo), dpp64<kDppXor1>(g.r), dpp64<kDppXor1>(g.r_lo)};
 }
+// The fields the fast requantization reads; amax and r (exact path only) are
+// exchanged when that path runs.
 __device__ __forceinline__ NewGroup swap_pair(const NewGroup& g) {
     NewGroup o;
     o.s = g.s;  // stored by the computing lane only
-    o.amax = dpp64<kDppXor1>(g.amax);
-    o.r = dpp64<kDppXor1>(g.r);
+    o.amax = 0.0;
+    o.r = 0.0;
     o.k = __builtin_bit_cast(float, dpp32<kDppXor1>(__builtin_bit_cast(uint32_t, g.k)));
     o.ia = __builtin_bit_cast(float, dpp32<kDppXor1>(__builtin_bit_cast(uint32_t, g.ia)));
     o.w = __builtin_bit_cast(float, dpp32<kDppXor1>(__builtin_bit_cast(uint32_t, g.w)));
@@ -1081,14 +1083,6 @@ __device__ __forceinline__ double exp2_dd(double h, double l) {
     return __builtin_amdgcn_ldexp(exp2_poly10((h - n) + l), cvt_i32_sat(n));
 }
 
-// a + b = s + err exactly.
-__device__ __forceinline__ double two_sum(double a, double b, double& err) {
-    const double s = a + b;
-    const double bb = s - a;
-    err = (a - (s - bb)) + (b - bb);
-    return s;
-}
-
 // (A + r x) in double-double for x = xh + xl and r = rh + rl, A = ah + al.
 __device__ __forceinline__ void fma_dd(double ah, double al, double rh, double rl, double xh, double xl,
                                        double& h, double& l) {
@@ -1374,6 +1368,7 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
 
     // ---- requantization constants (the lane pair splits the two moments)
     NewGroup nm, nv;
+    double own_amax = 0.0, own_r = 0.0;  // pair split: this lane's moment's exact-path fields
     if (pair) {
         const double amax_x = odd ? amax_v : amax_m, amin_x = odd ? amin_v : amin_m;
         double L, L_lo, Lm, Lm_lo;
@@ -1397,6 +1392,8 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
         const NewGroup other = swap_pair(mine);
         nm = odd ? other : mine;
         nv = odd ? mine : other;
+        own_amax = mine.amax;
+        own_r = mine.r;
         if (gvalid && (lane & (lpg - 1)) < 2) {
             double* sp = odd ? uniform_ptr(t.vs) : uniform_ptr(t.ms);
             float* kp = odd ? uniform_ptr(t.vk) : uniform_ptr(t.mk);
@@ -1437,6 +1434,13 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     if (nm.flags & kPoison) { am[0] = am[1] = am[2] = am[3] = 0u; }
     if (nv.flags & kPoison) { av[0] = av[1] = av[2] = av[3] = 0u; }
     if (__any((am[0] | am[1] | am[2] | am[3] | av[0] | av[1] | av[2] | av[3]) != 0u)) {
+        if (pair) {  // the other moment's exact-path fields, from the partner lane
+            const double oa = dpp64<kDppXor1>(own_amax), orr = dpp64<kDppXor1>(own_r);
+            nm.amax = odd ? oa : own_amax;
+            nm.r = odd ? orr : own_r;
+            nv.amax = odd ? own_amax : oa;
+            nv.r = odd ? own_r : orr;
+        }
         OldGroup pm, pv;
         parked_groups(pm, pv);
         redo_ambiguous<FM>(am, cm, pk.mq, pk, pm, nm, lq_m, ct.lqm[0], fm, c.c1, false, cf);
