@@ -1874,10 +1874,7 @@ __global__ __launch_bounds__(kBlock) void act_quantize_group_kernel(const uint16
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int lane = threadIdx.x & (kWave - 1);
     const int lpg = 1 << (lg2_group - 4);
-    for (int64_t tile = wave_id(); tile < tiles; tile += nw) {
-        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
-        uint32_t w[8];
-        act_load16(x, n, e0, w);
+    auto code = [&](int64_t e0, const uint32_t (&w)[8]) {
         const uint32_t am = group_umax(bf16_absmax_bits(w), lpg);
         uint32_t c[4];
         act_codes16<F>(w, am, c);
@@ -1886,6 +1883,22 @@ __global__ __launch_bounds__(kBlock) void act_quantize_group_kernel(const uint16
             const float amax = __builtin_bit_cast(float, am << 16);
             gp(s)[e0 >> lg2_group] = am >= 0x7F80u ? __builtin_nanf("") : (float)((double)amax / Fmt<F>::FPMAX);
         }
+    };
+    // two tiles per iteration: both tiles' loads are in flight together
+    int64_t tile = wave_id();
+    for (; tile + nw < tiles; tile += 2 * nw) {
+        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems, e1 = e0 + nw * kTile;
+        uint32_t w0[8], w1[8];
+        act_load16(x, n, e0, w0);
+        act_load16(x, n, e1, w1);
+        code(e0, w0);
+        code(e1, w1);
+    }
+    if (tile < tiles) {
+        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
+        uint32_t w[8];
+        act_load16(x, n, e0, w);
+        code(e0, w);
     }
 }
 
@@ -1941,13 +1954,26 @@ __global__ __launch_bounds__(kBlock) void act_quantize_tensor_kernel(const uint1
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t am = __builtin_amdgcn_readfirstlane(gp(acc)[0]);
-    for (int64_t tile = wave_id(); tile < tiles; tile += nw) {
-        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
-        uint32_t w[8];
-        act_load16(x, n, e0, w);
+    auto code = [&](int64_t e0, const uint32_t (&w)[8]) {
         uint32_t c[4];
         act_codes16<F>(w, am, c);
         act_store16(q, n, e0, c);
+    };
+    // two tiles per iteration: both tiles' loads are in flight together
+    int64_t tile = wave_id();
+    for (; tile + nw < tiles; tile += 2 * nw) {
+        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems, e1 = e0 + nw * kTile;
+        uint32_t w0[8], w1[8];
+        act_load16(x, n, e0, w0);
+        act_load16(x, n, e1, w1);
+        code(e0, w0);
+        code(e1, w1);
+    }
+    if (tile < tiles) {
+        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
+        uint32_t w[8];
+        act_load16(x, n, e0, w);
+        code(e0, w);
     }
 }
 
@@ -1963,6 +1989,15 @@ __global__ void act_finalize_kernel(uint32_t* acc) {
 
 // Codes and scales back to bf16: RN_bf16(decode(code) * s) with the fp32
 // product. lg2_group < 0: one scale for the tensor.
+// Exact value of byte B of a code word, by the hardware OCP converts.
+template <int F, int B>
+__device__ __forceinline__ float fp8_byte_value(uint32_t w) {
+    if constexpr (F == COAT_FMT_E4M3)
+        return __builtin_amdgcn_cvt_f32_fp8((int)w, B);
+    else
+        return __builtin_amdgcn_cvt_f32_bf8((int)w, B);
+}
+
 template <int F>
 __global__ __launch_bounds__(kBlock) void act_dequantize_kernel(const uint8_t* __restrict__ q,
                                                                 const float* __restrict__ s, int64_t n,
@@ -1970,11 +2005,7 @@ __global__ __launch_bounds__(kBlock) void act_dequantize_kernel(const uint8_t* _
     const int64_t tiles = (n + kTile - 1) / kTile;
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int lane = threadIdx.x & (kWave - 1);
-    for (int64_t tile = wave_id(); tile < tiles; tile += nw) {
-        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
-        if (e0 >= n) continue;
-        const float sc = gp(s)[lg2_group < 0 ? 0 : (e0 >> lg2_group)];
-        uint32_t c[4];
+    auto load = [&](int64_t e0, uint32_t (&c)[4]) {
         if (e0 + kLaneElems <= n) {
             const u32x4 v = *reinterpret_cast<const gu32x4*>(gp(q) + e0);
             c[0] = v.x; c[1] = v.y; c[2] = v.z; c[3] = v.w;
@@ -1985,14 +2016,19 @@ __global__ __launch_bounds__(kBlock) void act_dequantize_kernel(const uint8_t* _
             for (int i = 0; i < 16; ++i)
                 if (e0 + i < n) c[i >> 2] |= (uint32_t)gp(q)[e0 + i] << (8 * (i & 3));
         }
+    };
+    auto decode = [&](int64_t e0, const uint32_t (&c)[4]) {
+        if (e0 >= n) return;
+        const float sc = gp(s)[lg2_group < 0 ? 0 : (e0 >> lg2_group)];
         uint32_t o[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int j = 2 * i;
-            const float a = decode_value<F>(byte_of(c[j >> 2], j & 3)) * sc;
-            const float b = decode_value<F>(byte_of(c[(j + 1) >> 2], (j + 1) & 3)) * sc;
-            o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
-                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+        for (int i = 0; i < 4; ++i) {
+            const float v0 = fp8_byte_value<F, 0>(c[i]) * sc, v1 = fp8_byte_value<F, 1>(c[i]) * sc;
+            const float v2 = fp8_byte_value<F, 2>(c[i]) * sc, v3 = fp8_byte_value<F, 3>(c[i]) * sc;
+            o[2 * i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v0) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v1) << 16);
+            o[2 * i + 1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v2) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v3) << 16);
         }
         if (e0 + kLaneElems <= n) {
             gu32x4* p = reinterpret_cast<gu32x4*>(gp(x) + e0);
@@ -2003,6 +2039,22 @@ __global__ __launch_bounds__(kBlock) void act_dequantize_kernel(const uint8_t* _
             for (int i = 0; i < 16; ++i)
                 if (e0 + i < n) gp(x)[e0 + i] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
         }
+    };
+    // two tiles per iteration: both tiles' loads are in flight together
+    int64_t tile = wave_id();
+    for (; tile + nw < tiles; tile += 2 * nw) {
+        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems, e1 = e0 + nw * kTile;
+        uint32_t c0[4], c1[4];
+        load(e0, c0);
+        load(e1, c1);
+        decode(e0, c0);
+        decode(e1, c1);
+    }
+    if (tile < tiles) {
+        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
+        uint32_t c[4];
+        load(e0, c);
+        decode(e0, c);
     }
 }
 
