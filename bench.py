@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 PMC_FILE = os.path.join(ROOT, "profiles", "coat_step_multi_llama13b_pmc.json")
-KERNEL_SRC = os.path.join(ROOT, "fp8_optimizer_state_amd", "csrc", "coat_fp8.hip")
+# the sources the step kernel is built from (the activation codec is not one)
+KERNEL_SRCS = [os.path.join(ROOT, "fp8_optimizer_state_amd", "csrc", f) for f in ("coat_common.h", "coat_fp8.hip")]
 
 
 def log(msg: str) -> None:
@@ -41,8 +42,12 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the step kernel's source files, in order."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic(workload: str, n_launch_bytes: float):

@@ -6,7 +6,9 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "coat_fp8.hip")
+CSRC = os.path.join(PKG, "csrc")
+# the step kernels, state codec and core ABI; the activation codec
+SOURCES = [os.path.join(CSRC, "coat_fp8.hip"), os.path.join(CSRC, "act_fp8.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcoat_fp8.so")
 
@@ -21,10 +23,10 @@ HIPCC_FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Compile csrc/coat_fp8.hip into libcoat_fp8.so next to this file."""
+    """Compile the csrc/*.hip sources into libcoat_fp8.so next to this file."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I" + INCLUDE, "-o", tmp, SRC]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I" + INCLUDE, "-o", tmp, *SOURCES]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)

@@ -28,103 +28,11 @@
 //   * the AdamW update itself (master weights, bf16 copy) runs in fp32;
 //   * the multi-tensor kernel walks a descriptor table of a whole parameter
 //     list in one launch; tiles never span tensors.
-#include <hip/hip_runtime.h>
-
-#include <math.h>
-#include <stdint.h>
-#include <string.h>
-
 #include <vector>
 
-#include "coat_fp8.h"
+#include "coat_common.h"
 
 namespace {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) float gfloat;
-typedef __attribute__((address_space(1))) uint16_t gu16;
-typedef __attribute__((address_space(1))) uint8_t gu8;
-typedef __attribute__((address_space(1))) double gf64;
-typedef __attribute__((address_space(1))) f32x4 gf32x4;
-typedef __attribute__((address_space(1))) u32x4 gu32x4;
-
-constexpr int kWave = 64;
-constexpr int kLaneElems = 16;
-constexpr int kTile = kWave * kLaneElems;  // elements per wavefront tile
-constexpr int kBlock = 256;                // 4 wavefronts
-constexpr int kWavesPerBlock = kBlock / kWave;
-
-// Relative half-width of the window around an FP8 rounding midpoint inside
-// which a converted value is decided exactly (plain encoding, no transcendentals).
-constexpr float kAmbiguity = 0x1p-15f;
-
-// Window of the requantization fast path, per group: w = W0 + W1 k relative.
-// The fast path forms y = 2^(k log2(|x| / amax) + log2 fpmax) in fp32. Its
-// error: |x| / amax carries three fp32 roundings (<= 3 * 2^-24 relative, k
-// times that in y); v_log_f32 is accurate to about an ulp of its result, whose
-// magnitude times k stays below log2 R_fp8 (17.8 for E4M3, 31.8 for E5M2), so
-// k times that error stays below log2(R_fp8) * 2^-23; the fma adds half an
-// ulp of |z| <= 16; v_exp_f32 about an ulp. In total below ln 2 * (2^-23
-// log2 R_fp8 + 2^-20 + k * 2.6e-7) + 1.2e-7, i.e. 2.2e-6 + 1.8e-7 k (E4M3)
-// and 3.4e-6 + 1.8e-7 k (E5M2); measured maxima on gfx950 over 1.6e7 samples
-// per k sit at 55-70 % of that. W0 and W1 take twice the bound.
-constexpr float kAmbW1 = 3.6e-7f;
-
-template <typename T>
-__device__ __forceinline__ __attribute__((address_space(1))) T* gp(T* p) {
-    return (__attribute__((address_space(1))) T*)p;
-}
-
-// ------------------------------------------------------------------ formats
-
-template <int F>
-struct Fmt;
-
-template <>
-struct Fmt<COAT_FMT_E4M3> {
-    static constexpr int MB = 3;          // mantissa bits
-    static constexpr int BIAS = 7;
-    static constexpr int EMIN = -6;       // exponent of the smallest normal
-    static constexpr int TOP = 0x7E;      // largest finite magnitude code (448)
-    static constexpr double FPMAX = 448.0;
-    static constexpr float FPMAX_F = 448.0f;
-    static constexpr double LOG2_FPMAX = 0x1.19d5d9fd5010bp+3;  // log2(448)
-    static constexpr double LOG2_FPMAX_LO = 0x1.b332ac903a414p-52;  // its rounding error
-    static constexpr float LOG2_FPMAX_F = 0x1.19d5dap+3f;
-    static constexpr float AMB_W0 = 4.4e-6f;  // fast-path window, see kAmbW1
-    static constexpr double LOG2_RF = 0x1.1ceaecfea8086p+4;     // log2(448 / 2^-9)
-    __device__ static bool is_nan(int c) { return c == 0x7F; }
-    __device__ static bool is_inf(int) { return false; }
-};
-
-template <>
-struct Fmt<COAT_FMT_E5M2> {
-    static constexpr int MB = 2;
-    static constexpr int BIAS = 15;
-    static constexpr int EMIN = -14;
-    static constexpr int TOP = 0x7B;      // 57344
-    static constexpr double FPMAX = 57344.0;
-    static constexpr float FPMAX_F = 57344.0f;
-    static constexpr double LOG2_FPMAX = 0x1.f9d5d9fd5010bp+3;  // log2(57344)
-    static constexpr double LOG2_FPMAX_LO = 0x1.b332ac903a414p-52;  // its rounding error
-    static constexpr float LOG2_FPMAX_F = 0x1.f9d5dap+3f;
-    static constexpr float AMB_W0 = 6.8e-6f;  // fast-path window, see kAmbW1
-    static constexpr double LOG2_RF = 0x1.fceaecfea8086p+4;     // log2(57344 / 2^-16)
-    __device__ static bool is_nan(int c) { return c > 0x7C; }
-    __device__ static bool is_inf(int c) { return c == 0x7C; }
-};
-
-// Per-lane format constants, for code that serves both moments at once.
-struct FmtRT {
-    double fpmax, log2_fpmax, log2_fpmax_lo, log2_rf;
-    float fpmax_f, log2_fpmax_f, amb_w0;
-};
-template <int F>
-__device__ __forceinline__ FmtRT fmt_rt() {
-    using T = Fmt<F>;
-    return FmtRT{T::FPMAX, T::LOG2_FPMAX, T::LOG2_FPMAX_LO, T::LOG2_RF, T::FPMAX_F, T::LOG2_FPMAX_F, T::AMB_W0};
-}
 
 // ------------------------------------------------------------------ fp64 math
 //
@@ -291,43 +199,6 @@ __device__ __forceinline__ float next_down(float x) {  // x > 0 finite
     return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) - 1u);
 }
 
-// ------------------------------------------------------------------ cross-lane
-
-// Value of lane (lane ^ 1), (lane ^ 2), ... via DPP within a row of 16.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ double dpp64(double v) {
-    const uint64_t b = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = dpp32<CTRL>((uint32_t)b), hi = dpp32<CTRL>((uint32_t)(b >> 32));
-    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within 8
-constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within 16
-
-__device__ __forceinline__ double xlane64(double v, int d) {
-    switch (d) {
-        case 1: return dpp64<kDppXor1>(v);
-        case 2: return dpp64<kDppXor2>(v);
-        case 4: return dpp64<kDppHalfMirror>(v);
-        case 8: return dpp64<kDppMirror>(v);
-        default: return __shfl_xor(v, d, kWave);
-    }
-}
-__device__ __forceinline__ uint32_t xlane32(uint32_t v, int d) {
-    switch (d) {
-        case 1: return dpp32<kDppXor1>(v);
-        case 2: return dpp32<kDppXor2>(v);
-        case 4: return dpp32<kDppHalfMirror>(v);
-        case 8: return dpp32<kDppMirror>(v);
-        default: return (uint32_t)__shfl_xor((int)v, d, kWave);
-    }
-}
-
 // All-reduce over the `lanes` lanes (a power of two, aligned) owning a group.
 // After the first steps the sub-blocks agree, so the mirror permutations pair
 // every lane with one of the other half, as an xor would.
@@ -338,56 +209,6 @@ __device__ __forceinline__ double group_max(double v, int lanes) {
 __device__ __forceinline__ double group_min(double v, int lanes) {
     for (int d = 1; d < lanes; d <<= 1) v = vmin(v, xlane64(v, d));
     return v;
-}
-__device__ __forceinline__ uint32_t group_or(uint32_t v, int lanes) {
-    for (int d = 1; d < lanes; d <<= 1) v |= xlane32(v, d);
-    return v;
-}
-
-// ------------------------------------------------------------------ FP8 codec
-
-// Magnitude code of y >= 0 (not NaN): nearest FP8 value, ties to even,
-// saturating at the largest finite value. Exact for every fp64 input.
-template <int F>
-__device__ uint32_t encode_mag_exact(double y) {
-    using T = Fmt<F>;
-    if (!(y < T::FPMAX)) return T::TOP;
-    if (y == 0.0) return 0;
-    int e = __builtin_amdgcn_frexp_exp(y) - 1;  // y in [2^e, 2^(e+1))
-    int ee = e > T::EMIN ? e : T::EMIN;
-    double nq = __builtin_rint(__builtin_amdgcn_ldexp(y, T::MB - ee));  // quanta of 2^(ee-MB)
-    int code = ((ee + T::BIAS - 1) << T::MB) + (int)nq;
-    return (uint32_t)(code < T::TOP ? code : T::TOP);
-}
-
-// Two fp32 values -> two FP8 codes in the low (HI = false) or high half of `old`.
-template <int F, bool HI>
-__device__ __forceinline__ uint32_t cvt_pk(float a, float b, uint32_t old) {
-    if constexpr (F == COAT_FMT_E4M3)
-        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
-    else
-        return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, HI);
-}
-
-// Exact value of a magnitude code (finite codes only).
-template <int F>
-__device__ double value_of(int c) {
-    using T = Fmt<F>;
-    const int e = c >> T::MB, m = c & ((1 << T::MB) - 1);
-    return e ? __builtin_amdgcn_ldexp(1.0 + (double)m / (double)(1 << T::MB), e - T::BIAS)
-             : __builtin_amdgcn_ldexp((double)m, T::EMIN - T::MB);
-}
-
-// Exact value of an FP8 code.
-template <int F>
-__device__ float decode_value(uint32_t code) {
-    using T = Fmt<F>;
-    const int c = code & 0x7F;
-    float mag;
-    if (T::is_nan(c)) mag = __builtin_nanf("");
-    else if (T::is_inf(c)) mag = __builtin_inff();
-    else mag = (float)value_of<F>(c);
-    return (code & 0x80) ? -mag : mag;
 }
 
 // Per-block constant tables, one row per moment:
@@ -872,7 +693,6 @@ __device__ __forceinline__ double dequant_mag(uint32_t w, int i, const OldGroup&
     return __builtin_amdgcn_ldexp(exp2_poly10((u - n) + og.a_lo), cvt_i32_sat(n));
 }
 
-__device__ __forceinline__ uint32_t byte_of(uint32_t w, int i) { return (w >> (8 * i)) & 0xFFu; }
 
 __device__ __forceinline__ uint32_t select4(int i, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
     return i == 0 ? a0 : (i == 1 ? a1 : (i == 2 ? a2 : a3));
@@ -1464,9 +1284,6 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     }
 }
 
-__device__ __forceinline__ int64_t wave_id() {
-    return (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-}
 
 // Which tiles a step kernel launch covers.
 constexpr int kPhaseFull = 1;     // tiles wholly inside their tensor
@@ -1743,356 +1560,9 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const uint8_t* __restric
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += nw) y[i] = decode_value<F>(q[i]);
 }
 
-// ------------------------------------------------------------------ activation codec
-//
-// Article, section "Solution: mixed-granularity FP8 precision flow": layer
-// inputs are kept in FP8 for the backward pass, with a quantization
-// granularity that differs between layers. Plain absmax scaling of bf16
-// values with one fp32 scale per tensor or per group of G consecutive values:
-// s = RN32(amax / fpmax), code = encode(RN32(x / s)) (the sign alone when
-// s = 0), value = RN_bf16(RN32(decode(code) s)); a tensor or group holding a
-// NaN or Inf gets s = NaN and every code 0x7F.
-//
-// The codes come from x * (1 / s) through the hardware converts; x * (1/s)
-// is within 2 ulp of RN32(x / s), so only a value within kAmbiguity of an
-// FP8 rounding midpoint can round differently, and those are redone from the
-// exact quotient.
-
-// bf16 magnitude bits of 16 values (two 16-byte words per 8 values) -> max.
-__device__ __forceinline__ uint32_t bf16_absmax_bits(const uint32_t (&w)[8]) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t a = w[i] & 0x7FFF7FFFu;
-        const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
-        m = m > lo ? m : lo;
-        m = m > hi ? m : hi;
-    }
-    return m;
-}
-
-__device__ __forceinline__ uint32_t group_umax(uint32_t v, int lanes) {
-    for (int d = 1; d < lanes; d <<= 1) {
-        const uint32_t o = xlane32(v, d);
-        v = v > o ? v : o;
-    }
-    return v;
-}
-
-// Codes of the 16 bf16 values in w (value i in half i & 1 of word i >> 1) for
-// a group with magnitude bits `amax_bits`; returns the four code words.
-template <int F>
-__device__ __forceinline__ void act_codes16(const uint32_t (&w)[8], uint32_t amax_bits, uint32_t (&out)[4]) {
-    using T = Fmt<F>;
-    if (amax_bits >= 0x7F80u) {  // Inf or NaN in the group
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = 0x7F7F7F7Fu;
-        return;
-    }
-    const float amax = __builtin_bit_cast(float, amax_bits << 16);
-    const float sc = (float)((double)amax / T::FPMAX);
-    if (sc == 0.0f) {  // all zero: the sign alone
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t c = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int j = 4 * i + b;
-                c |= ((w[j >> 1] >> (16 * (j & 1) + 15)) & 1u) << (8 * b + 7);
-            }
-            out[i] = c;
-        }
-        return;
-    }
-    // A subnormal scale (amax below 2^-117 or so) has a reciprocal beyond the
-    // fp32 range: every element of such a group takes the exact path.
-    const uint32_t all = sc < 0x1p-126f ? 0x80808080u : 0u;
-    const float r = 1.0f / sc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float x[4], lo[4], hi[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int j = 4 * i + b;
-            x[b] = __builtin_bit_cast(float, (j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16));
-            const float a = __builtin_fabsf(x[b]) * r;
-            lo[b] = __builtin_copysignf(__builtin_fminf(a * (1.0f - kAmbiguity), T::FPMAX_F), x[b]);
-            hi[b] = __builtin_fminf(a * (1.0f + kAmbiguity), T::FPMAX_F);
-        }
-        uint32_t wl = cvt_pk<F, false>(lo[0], lo[1], 0u);
-        wl = cvt_pk<F, true>(lo[2], lo[3], wl);
-        uint32_t wh = cvt_pk<F, false>(hi[0], hi[1], 0u);
-        wh = cvt_pk<F, true>(hi[2], hi[3], wh);
-        const uint32_t d = ((((wl ^ wh) & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u) | all;
-        if (d) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                if ((d >> (8 * b + 7)) & 1u) {
-                    const float y = (float)((double)x[b] / (double)sc);  // RN32(x / s)
-                    const uint32_t c = (__builtin_signbit(x[b]) ? 0x80u : 0u) |
-                                       encode_mag_exact<F>(__builtin_fabs((double)y));
-                    wl = (wl & ~(0xFFu << (8 * b))) | (c << (8 * b));
-                }
-            }
-        }
-        out[i] = wl;
-    }
-}
-
-// Loads the lane's 16 bf16 values of a tile (zeros past n).
-__device__ __forceinline__ void act_load16(const uint16_t* x, int64_t n, int64_t e0, uint32_t (&w)[8]) {
-    if (e0 + kLaneElems <= n) {
-        const gu32x4* p = reinterpret_cast<const gu32x4*>(gp(x) + e0);
-        const u32x4 a = p[0], b = p[1];
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = 0u;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (e0 + i < n) w[i >> 1] |= (uint32_t)gp(x)[e0 + i] << (16 * (i & 1));
-    }
-}
-
-__device__ __forceinline__ void act_store16(uint8_t* q, int64_t n, int64_t e0, const uint32_t (&c)[4]) {
-    if (e0 + kLaneElems <= n) {
-        *reinterpret_cast<gu32x4*>(gp(q) + e0) = u32x4{c[0], c[1], c[2], c[3]};
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (e0 + i < n) gp(q)[e0 + i] = (uint8_t)byte_of(c[i >> 2], i & 3);
-    }
-}
-
-// Per group of G = 2^lg2_group (16 .. 1024): a group spans G / 16 lanes.
-template <int F>
-__global__ __launch_bounds__(kBlock) void act_quantize_group_kernel(const uint16_t* __restrict__ x, int64_t n,
-                                                                    int lg2_group, uint8_t* __restrict__ q,
-                                                                    float* __restrict__ s) {
-    const int64_t tiles = (n + kTile - 1) / kTile;
-    const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int lpg = 1 << (lg2_group - 4);
-    auto code = [&](int64_t e0, const uint32_t (&w)[8]) {
-        const uint32_t am = group_umax(bf16_absmax_bits(w), lpg);
-        uint32_t c[4];
-        act_codes16<F>(w, am, c);
-        act_store16(q, n, e0, c);
-        if ((lane & (lpg - 1)) == 0 && e0 < n) {
-            const float amax = __builtin_bit_cast(float, am << 16);
-            gp(s)[e0 >> lg2_group] = am >= 0x7F80u ? __builtin_nanf("") : (float)((double)amax / Fmt<F>::FPMAX);
-        }
-    };
-    // two tiles per iteration: both tiles' loads are in flight together
-    int64_t tile = wave_id();
-    for (; tile + nw < tiles; tile += 2 * nw) {
-        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems, e1 = e0 + nw * kTile;
-        uint32_t w0[8], w1[8];
-        act_load16(x, n, e0, w0);
-        act_load16(x, n, e1, w1);
-        code(e0, w0);
-        code(e1, w1);
-    }
-    if (tile < tiles) {
-        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
-        uint32_t w[8];
-        act_load16(x, n, e0, w);
-        code(e0, w);
-    }
-}
-
-// Per tensor: acc[0] = 0, then the magnitude bits' maximum, then the codes,
-// then acc[0] = the scale (acc is the caller's scale word).
-__global__ void act_zero_kernel(uint32_t* acc) {
-    if (threadIdx.x == 0) gp(acc)[0] = 0u;
-}
-
-// One atomic per block (atomics on one word serialize); four tiles per
-// iteration keep more loads in flight per wavefront.
-__global__ __launch_bounds__(kBlock) void act_absmax_kernel(const uint16_t* __restrict__ x, int64_t n,
-                                                            uint32_t* acc) {
-    __shared__ uint32_t wmax[kWavesPerBlock];
-    const int64_t tiles = (n + kTile - 1) / kTile;
-    const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t off = (int64_t)lane * kLaneElems;
-    uint32_t m = 0;
-    int64_t tile = wave_id();
-    for (; tile + 3 * nw < tiles; tile += 4 * nw) {
-        uint32_t w0[8], w1[8], w2[8], w3[8];
-        act_load16(x, n, tile * kTile + off, w0);
-        act_load16(x, n, (tile + nw) * kTile + off, w1);
-        act_load16(x, n, (tile + 2 * nw) * kTile + off, w2);
-        act_load16(x, n, (tile + 3 * nw) * kTile + off, w3);
-        const uint32_t a = bf16_absmax_bits(w0), b = bf16_absmax_bits(w1);
-        const uint32_t c = bf16_absmax_bits(w2), d = bf16_absmax_bits(w3);
-        const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
-        const uint32_t v = ab > cd ? ab : cd;
-        m = m > v ? m : v;
-    }
-    for (; tile < tiles; tile += nw) {
-        uint32_t w[8];
-        act_load16(x, n, tile * kTile + off, w);
-        const uint32_t v = bf16_absmax_bits(w);
-        m = m > v ? m : v;
-    }
-    m = group_umax(m, kWave);
-    if (lane == 0) wmax[threadIdx.x / kWave] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t bm = 0;
-        for (int i = 0; i < kWavesPerBlock; ++i) bm = bm > wmax[i] ? bm : wmax[i];
-        atomicMax(acc, bm);
-    }
-}
-
-template <int F>
-__global__ __launch_bounds__(kBlock) void act_quantize_tensor_kernel(const uint16_t* __restrict__ x, int64_t n,
-                                                                     const uint32_t* acc, uint8_t* __restrict__ q) {
-    const int64_t tiles = (n + kTile - 1) / kTile;
-    const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t am = __builtin_amdgcn_readfirstlane(gp(acc)[0]);
-    auto code = [&](int64_t e0, const uint32_t (&w)[8]) {
-        uint32_t c[4];
-        act_codes16<F>(w, am, c);
-        act_store16(q, n, e0, c);
-    };
-    // two tiles per iteration: both tiles' loads are in flight together
-    int64_t tile = wave_id();
-    for (; tile + nw < tiles; tile += 2 * nw) {
-        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems, e1 = e0 + nw * kTile;
-        uint32_t w0[8], w1[8];
-        act_load16(x, n, e0, w0);
-        act_load16(x, n, e1, w1);
-        code(e0, w0);
-        code(e1, w1);
-    }
-    if (tile < tiles) {
-        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
-        uint32_t w[8];
-        act_load16(x, n, e0, w);
-        code(e0, w);
-    }
-}
-
-template <int F>
-__global__ void act_finalize_kernel(uint32_t* acc) {
-    if (threadIdx.x == 0) {
-        const uint32_t am = gp(acc)[0];
-        const float amax = __builtin_bit_cast(float, am << 16);
-        const float sc = am >= 0x7F80u ? __builtin_nanf("") : (float)((double)amax / Fmt<F>::FPMAX);
-        gp(acc)[0] = __builtin_bit_cast(uint32_t, sc);
-    }
-}
-
-// Codes and scales back to bf16: RN_bf16(decode(code) * s) with the fp32
-// product. lg2_group < 0: one scale for the tensor.
-// Exact value of byte B of a code word, by the hardware OCP converts.
-template <int F, int B>
-__device__ __forceinline__ float fp8_byte_value(uint32_t w) {
-    if constexpr (F == COAT_FMT_E4M3)
-        return __builtin_amdgcn_cvt_f32_fp8((int)w, B);
-    else
-        return __builtin_amdgcn_cvt_f32_bf8((int)w, B);
-}
-
-template <int F>
-__global__ __launch_bounds__(kBlock) void act_dequantize_kernel(const uint8_t* __restrict__ q,
-                                                                const float* __restrict__ s, int64_t n,
-                                                                int lg2_group, uint16_t* __restrict__ x) {
-    const int64_t tiles = (n + kTile - 1) / kTile;
-    const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
-    const int lane = threadIdx.x & (kWave - 1);
-    auto load = [&](int64_t e0, uint32_t (&c)[4]) {
-        if (e0 + kLaneElems <= n) {
-            const u32x4 v = *reinterpret_cast<const gu32x4*>(gp(q) + e0);
-            c[0] = v.x; c[1] = v.y; c[2] = v.z; c[3] = v.w;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) c[i] = 0u;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (e0 + i < n) c[i >> 2] |= (uint32_t)gp(q)[e0 + i] << (8 * (i & 3));
-        }
-    };
-    auto decode = [&](int64_t e0, const uint32_t (&c)[4]) {
-        if (e0 >= n) return;
-        const float sc = gp(s)[lg2_group < 0 ? 0 : (e0 >> lg2_group)];
-        uint32_t o[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float v0 = fp8_byte_value<F, 0>(c[i]) * sc, v1 = fp8_byte_value<F, 1>(c[i]) * sc;
-            const float v2 = fp8_byte_value<F, 2>(c[i]) * sc, v3 = fp8_byte_value<F, 3>(c[i]) * sc;
-            o[2 * i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v0) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v1) << 16);
-            o[2 * i + 1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v2) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v3) << 16);
-        }
-        if (e0 + kLaneElems <= n) {
-            gu32x4* p = reinterpret_cast<gu32x4*>(gp(x) + e0);
-            p[0] = u32x4{o[0], o[1], o[2], o[3]};
-            p[1] = u32x4{o[4], o[5], o[6], o[7]};
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (e0 + i < n) gp(x)[e0 + i] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
-        }
-    };
-    // two tiles per iteration: both tiles' loads are in flight together
-    int64_t tile = wave_id();
-    for (; tile + nw < tiles; tile += 2 * nw) {
-        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems, e1 = e0 + nw * kTile;
-        uint32_t c0[4], c1[4];
-        load(e0, c0);
-        load(e1, c1);
-        decode(e0, c0);
-        decode(e1, c1);
-    }
-    if (tile < tiles) {
-        const int64_t e0 = tile * kTile + (int64_t)lane * kLaneElems;
-        uint32_t c[4];
-        load(e0, c);
-        decode(e0, c);
-    }
-}
-
 // ------------------------------------------------------------------ host side
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-int lg2_group_of(int32_t group) {
-    if (group < 16 || group > 1024 || (group & (group - 1)) != 0) return -1;
-    int l = 0;
-    while ((1 << l) < group) ++l;
-    return l;
-}
-
-bool fmt_ok(int32_t fmt) {
-    const int base = fmt & 0xFF;
-    return (base == COAT_FMT_E4M3 || base == COAT_FMT_E5M2) && (fmt & ~(0xFF | COAT_FMT_NO_EXPAND)) == 0;
-}
-
-int device_cus() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return 256;
-    return cus;
-}
-
-// Blocks for a grid-stride launch over `waves` wavefront tiles: enough to fill
-// every CU `per_cu` times, never more than there is work.
-unsigned grid_for(int64_t waves, int per_cu) {
-    const int64_t want = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t cap = (int64_t)device_cus() * per_cu;
-    int64_t b = want < cap ? want : cap;
-    return (unsigned)(b < 1 ? 1 : b);
-}
-
-// Many more blocks than fit on a CU at once (3 here): blocks are handed to CUs
+// Many more blocks than fit on a CU at once (3 or 4 here): blocks are handed to CUs
 // as earlier ones finish, which evens out the load across CUs and XCDs; beyond
 // about a hundred per CU each block's table set-up starts to cost more.
 constexpr int kStepBlocksPerCU = 128;
@@ -2133,7 +1603,6 @@ int check_tensor(const TensorRef& t) {
     return COAT_OK;
 }
 
-int launch_status() { return hipGetLastError() == hipSuccess ? COAT_OK : COAT_EHIP; }
 
 // Groups of 128 and more: the whole tiles run in the table kernel, then a
 // direct-path launch covers any partial tiles. Otherwise one direct-path launch.
@@ -2364,54 +1833,6 @@ int coat_fp8_decode(const uint8_t* q, int64_t n, int32_t fmt, float* y, coat_str
     const unsigned grid = grid_for((n + kWave - 1) / kWave, 16);
     if (fmt == COAT_FMT_E4M3) hipLaunchKernelGGL(decode_kernel<COAT_FMT_E4M3>, dim3(grid), dim3(kBlock), 0, st, q, n, y);
     else hipLaunchKernelGGL(decode_kernel<COAT_FMT_E5M2>, dim3(grid), dim3(kBlock), 0, st, q, n, y);
-    return launch_status();
-}
-
-int coat_fp8_act_quantize(const uint16_t* x, int64_t n, int32_t group, int32_t fmt, uint8_t* q, float* scale,
-                          coat_stream_t stream) {
-    const int lg = group == 0 ? 0 : lg2_group_of(group);
-    if (n < 0 || lg < 0 || (fmt != COAT_FMT_E4M3 && fmt != COAT_FMT_E5M2)) return COAT_EINVAL;
-    if (n == 0) return COAT_OK;
-    if (!x || !q || !scale) return COAT_EINVAL;
-    if (!aligned16(x) || !aligned16(q) || !aligned(scale, 4)) return COAT_EALIGN;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const int64_t tiles = (n + kTile - 1) / kTile;
-    const unsigned grid = grid_for(tiles, 16);
-    const bool e4 = fmt == COAT_FMT_E4M3;
-    if (group != 0) {
-        if (e4) hipLaunchKernelGGL(act_quantize_group_kernel<COAT_FMT_E4M3>, dim3(grid), dim3(kBlock), 0, st, x, n, lg, q, scale);
-        else hipLaunchKernelGGL(act_quantize_group_kernel<COAT_FMT_E5M2>, dim3(grid), dim3(kBlock), 0, st, x, n, lg, q, scale);
-        return launch_status();
-    }
-    uint32_t* acc = reinterpret_cast<uint32_t*>(scale);
-    hipLaunchKernelGGL(act_zero_kernel, dim3(1), dim3(kWave), 0, st, acc);
-    hipLaunchKernelGGL(act_absmax_kernel, dim3(grid_for(tiles, 2)), dim3(kBlock), 0, st, x, n, acc);
-    if (e4) {
-        hipLaunchKernelGGL(act_quantize_tensor_kernel<COAT_FMT_E4M3>, dim3(grid), dim3(kBlock), 0, st, x, n,
-                           (const uint32_t*)acc, q);
-        hipLaunchKernelGGL(act_finalize_kernel<COAT_FMT_E4M3>, dim3(1), dim3(kWave), 0, st, acc);
-    } else {
-        hipLaunchKernelGGL(act_quantize_tensor_kernel<COAT_FMT_E5M2>, dim3(grid), dim3(kBlock), 0, st, x, n,
-                           (const uint32_t*)acc, q);
-        hipLaunchKernelGGL(act_finalize_kernel<COAT_FMT_E5M2>, dim3(1), dim3(kWave), 0, st, acc);
-    }
-    return launch_status();
-}
-
-int coat_fp8_act_dequantize(const uint8_t* q, const float* scale, int64_t n, int32_t group, int32_t fmt,
-                            uint16_t* x, coat_stream_t stream) {
-    const int lg = group == 0 ? 0 : lg2_group_of(group);
-    if (n < 0 || lg < 0 || (fmt != COAT_FMT_E4M3 && fmt != COAT_FMT_E5M2)) return COAT_EINVAL;
-    if (n == 0) return COAT_OK;
-    if (!x || !q || !scale) return COAT_EINVAL;
-    if (!aligned16(x) || !aligned16(q) || !aligned(scale, 4)) return COAT_EALIGN;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const unsigned grid = grid_for((n + kTile - 1) / kTile, 16);
-    const int lgs = group == 0 ? -1 : lg;
-    if (fmt == COAT_FMT_E4M3)
-        hipLaunchKernelGGL(act_dequantize_kernel<COAT_FMT_E4M3>, dim3(grid), dim3(kBlock), 0, st, q, scale, n, lgs, x);
-    else
-        hipLaunchKernelGGL(act_dequantize_kernel<COAT_FMT_E5M2>, dim3(grid), dim3(kBlock), 0, st, q, scale, n, lgs, x);
     return launch_status();
 }
 
