@@ -266,7 +266,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the step shards by whole groups with no exchange; see the design notes)",
+              "(the step shards by whole groups with no exchange between GPUs)",
               file=sys.stderr)
         return 2
     if args.sweep:

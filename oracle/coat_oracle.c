@@ -26,7 +26,7 @@
  *   - maplevalley.com.cn FP8 guide, section "format choice": E4M3 is
  *     1 sign + 4 exponent + 3 mantissa bits, E5M2 is 1 + 5 + 2.
  *
- * Readings the pages leave open (all listed in the design notes):
+ * Readings the pages leave open:
  *   - decode is OCP E4M3FN (bias 7, max 448, NaN 0x7F/0xFF, no Inf) and OCP
  *     E5M2 (bias 15, max 57344, Inf 0x7C/0xFC, NaN 0x7D-0x7F/0xFD-0xFF);
  *   - R_fp8 = max finite / min subnormal (229376 for E4M3, matching the page's
