@@ -18,7 +18,7 @@
  *     function f is applied before quantizing; k is computed on the fly, one k
  *     per group, and k > 1 widens the group's range toward the FP8 range.
  *     The page's formula for f is lost; f(x) = sign(x)|x|^k with
- *     k = ln(R_fp8) / ln(R_x) is the reading this build fixes.
+ *     k = ln(R_fp8) / ln(R_x) is the reading taken here.
  *   - same page: E4M3 suits the first moment better than E5M2; for the second
  *     moment both are close once expansion is applied.
  *   - zhanchiexpo.com mirror of the same article: the states are quantized

@@ -1,6 +1,6 @@
 """Shared helpers of the GPU parity tests: seeded inputs, oracle runs, tolerances.
 
-Tolerances (the build's stated bar): per-group s and k within 1e-5 relative;
+Tolerances: per-group s and k within 1e-5 relative;
 fp32 master weights within 1e-5 relative or 1e-8 absolute; FP8 codes identical
 except for at most one code step on at most 1e-4 of the elements.
 """

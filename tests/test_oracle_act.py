@@ -5,7 +5,7 @@ forms.
 
 Article, section "Solution: mixed-granularity FP8 precision flow": layer
 inputs are kept in FP8 for the backward pass with a granularity that differs
-between layers. The formula is this build's reading: s = RN32(amax / fpmax),
+between layers. The formula is the reading taken here: s = RN32(amax / fpmax),
 code = encode(RN32(x / s)), value = RN_bf16(RN32(decode(code) * s)).
 """
 import numpy as np
