@@ -79,12 +79,15 @@ def step_kwargs(fm, fv):
                 weight_decay=h["wd"], step=h["step"])
 
 
-def test_mixed_list_equals_single_calls(coat):
-    """Tiny, empty, ragged and multi-tile tensors in one launch; the result is
-    bit-identical to one single-tensor call per tensor and matches the oracle."""
-    sizes = [768, 0, 1, 17, 2304, 1024 * 5 + 3, 50, 128 * 33, 4096 + 1000, 16]
-    G, fm, fv = 128, E4, E5
-    log(f"test_mixed_list_equals_single_calls sizes={sizes}")
+@pytest.mark.parametrize("G,fm,fv", [(16, E4, E4), (32, E4, E5), (64, E5, E4), (128, E4, E5), (128, E5, E5),
+                                     (256, E4, E5), (512, E5, E4), (1024, E4, E4)])
+def test_mixed_list_equals_single_calls(coat, G, fm, fv):
+    """Tiny, empty, ragged and multi-tile tensors in one launch (the multi-tensor
+    kernels specialized for each group size, and the partial tiles' kernel);
+    the result is bit-identical to one single-tensor call per tensor and
+    matches the oracle."""
+    sizes = [768, 0, 1, 17, 2304, 1024 * 5 + 3, 50, 128 * 33, 4096 + 1000, 16, 1024 * 9 + 512 + 7]
+    log(f"test_mixed_list_equals_single_calls G={G} fm={fm} fv={fv} sizes={sizes}")
     st, host = build_list(coat, sizes, G, fm, fv, seed=41)
     st2, _ = build_list(coat, sizes, G, fm, fv, seed=41)
     st.step(**step_kwargs(fm, fv))
@@ -99,7 +102,7 @@ def test_mixed_list_equals_single_calls(coat):
         for key in x:
             assert np.array_equal(x[key], y[key], equal_nan=True), key
     ref = oracle_list([h for h, n in zip(host, sizes) if n], G, fm, fv)
-    compare(concat([x for x, n in zip(a, sizes) if n]), concat(ref), "mixed-list")
+    compare(concat([x for x, n in zip(a, sizes) if n]), concat(ref), f"mixed-list G={G}")
 
 
 def test_unplanned_entry_point(coat):
