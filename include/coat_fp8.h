@@ -130,8 +130,10 @@ int coat_multi_plan_init(coat_multi_plan* plan, const coat_tensor* tensors, int3
                          void* workspace, size_t workspace_bytes, coat_stream_t stream);
 
 /*
- * One step over every tensor of a plan, in one kernel launch (asynchronous).
- * The result equals calling coat_fp8_adamw_step on each tensor in turn.
+ * One step over every tensor of a plan, asynchronous: one kernel launch over
+ * the whole list (for G >= 128 a second, small one when some tensor ends
+ * inside a 1024-element tile: its last tile). The result equals calling
+ * coat_fp8_adamw_step on each tensor in turn, bit for bit.
  */
 int coat_fp8_adamw_step_planned(const coat_multi_plan* plan, int32_t group, int32_t fmt_m,
                                 int32_t fmt_v, float lr, float beta1, float beta2, float eps,
