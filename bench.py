@@ -247,7 +247,8 @@ def cpu_baseline(wl, per_tensor: int = 229376) -> dict:
         pass
     return {"value": n / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"first {per_tensor} elements of each of the {len(wl.sizes)} tensors "
-                      f"({n} params), one step, single-threaded fp64 C oracle; {dt:.1f} s on {cpu}",
+                      f"({n} params), one step, single-threaded fp64 C oracle; {dt:.1f} s on {cpu} "
+                      f"({os.cpu_count()} hardware threads on the host)",
             "seconds": dt}
 
 
@@ -264,6 +265,9 @@ def main() -> int:
                     help="time and measure the codec error of every group size / format / expansion variant")
     ap.add_argument("--act", action="store_true", help="time the FP8 activation codec instead of the step")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py needs --steps >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the step shards by whole groups with no exchange between GPUs)",
@@ -316,16 +320,19 @@ def main() -> int:
     log(f"warmup {args.warmup} done")
 
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event between consecutive launches as well, for the per-step spread
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         st.step(step=step, **hy)
         step += 1
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    ms_median, ms_min = per_step[len(per_step) // 2], per_step[0]
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (median {ms_median:.3f}, min {ms_min:.3f})")
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.float32, device=dev)  # 4 GiB read, 4 GiB written
@@ -357,6 +364,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": ms_median,
+        "ms_per_step_min": ms_min,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
