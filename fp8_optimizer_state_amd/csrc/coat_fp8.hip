@@ -1326,11 +1326,45 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAB ? 4 
     }
 }
 
+// The whole tiles of a multi-tensor launch. Each block takes one contiguous
+// run of the global tile index space, its waves interleaved so that a block
+// streams adjacent tiles together, and reads a tensor's descriptor once per
+// run segment rather than once per tile (the descriptor table is too large
+// for the scalar cache, and each of its reads sits on the path to the tile's
+// loads). f(t, tile) gets the tensor and the tile's index within it.
+template <typename F>
+__device__ __forceinline__ void block_full_tiles(const TensorRef* __restrict__ ts, const int64_t* __restrict__ fb,
+                                                 int count, int64_t full, F&& f) {
+    const int64_t per = (full + gridDim.x - 1) / gridDim.x;
+    const int64_t b0 = (int64_t)blockIdx.x * per;
+    const int64_t b1 = b0 + per < full ? b0 + per : full;
+    int64_t tile = b0 + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (tile >= b1) return;
+    // the tensor holding `tile`: fb[lo] <= tile < fb[hi], fb[0] = 0, fb[count] = full
+    int lo = 0, hi = count;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (fb[mid] <= tile) lo = mid;
+        else hi = mid;
+    }
+    int cur = lo;
+    while (tile < b1) {
+        const int64_t tb = fb[cur], te = fb[cur + 1];
+        if (tile >= te) {  // tile < full keeps cur + 1 <= count
+            ++cur;
+            continue;
+        }
+        const TensorRef t = ts[cur];
+        const int64_t stop = te < b1 ? te : b1;
+        for (; tile < stop; tile += kWavesPerBlock) f(t, tile - tb);
+    }
+}
+
 // Multi-tensor: descriptors, the prefix of full tiles per tensor (count + 1
 // entries) and the list of tensors with a partial last tile live in device
-// workspace. Each wavefront strides over the global full-tile index space,
-// walking the prefix forward to find the tensor of its tile; then the partial
-// tiles take the general path. Phases and TAB as for the single kernel.
+// workspace. The whole tiles are split into one contiguous run per block
+// (block_full_tiles); then the partial tiles take the general path, one per
+// wavefront. Phases and TAB as for the single kernel.
 template <int FM, int FV, bool TAB, int LG>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAB ? 4 : 3, TAB ? 4 : 3))) void step_multi_kernel(
     const TensorRef* __restrict__ ts, const int64_t* __restrict__ full_begin, const int32_t* __restrict__ partial,
@@ -1344,21 +1378,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAB ? 4 
     const int64_t full = full_begin[count];
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     if (phases & kPhaseFull) {
-        int cur = 0;
         if (lg >= 5) {
-            for (int64_t tile = wave_id(); tile < full; tile += nw) {
-                while (tile >= full_begin[cur + 1]) ++cur;
+            block_full_tiles(ts, full_begin, count, full, [&](const TensorRef& t, int64_t tile) {
                 TileIn in;
-                load_full_tile<TAB>(ts[cur], tile - full_begin[cur], lg, in);
-                step_tile<FM, FV, true, TAB, LG>(ts[cur], tile - full_begin[cur], c, ct, wl, in);
-            }
+                load_full_tile<TAB>(t, tile, lg, in);
+                step_tile<FM, FV, true, TAB, LG>(t, tile, c, ct, wl, in);
+            });
         } else if constexpr (!TAB) {
-            for (int64_t tile = wave_id(); tile < full; tile += nw) {
-                while (tile >= full_begin[cur + 1]) ++cur;
+            block_full_tiles(ts, full_begin, count, full, [&](const TensorRef& t, int64_t tile) {
                 TileIn in;
-                load_tile(ts[cur], tile - full_begin[cur], lg, in);
-                step_tile<FM, FV, false, false, LG>(ts[cur], tile - full_begin[cur], c, ct, wl, in);
-            }
+                load_tile(t, tile, lg, in);
+                step_tile<FM, FV, false, false, LG>(t, tile, c, ct, wl, in);
+            });
         }
     }
     if constexpr (!TAB) {
@@ -1563,9 +1594,11 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const uint8_t* __restric
 // ------------------------------------------------------------------ host side
 
 // Many more blocks than fit on a CU at once (3 or 4 here): blocks are handed to CUs
-// as earlier ones finish, which evens out the load across CUs and XCDs; beyond
-// about a hundred per CU each block's table set-up starts to cost more.
-constexpr int kStepBlocksPerCU = 128;
+// as earlier ones finish, which evens out the load across CUs and XCDs (some
+// run several per cent slower than others: with exactly one resident round of
+// blocks the 13B step takes 10 % longer); beyond a few hundred per CU each
+// block's table set-up starts to cost more than the finer balance gains.
+constexpr int kStepBlocksPerCU = 256;
 
 bool finite_f(float x) { return x == x && x - x == 0.0f; }
 
