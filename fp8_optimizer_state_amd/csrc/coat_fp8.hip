@@ -1364,9 +1364,12 @@ __device__ __forceinline__ void block_full_tiles(const TensorRef* __restrict__ t
 // entries) and the list of tensors with a partial last tile live in device
 // workspace. The whole tiles are split into one contiguous run per block
 // (block_full_tiles); then the partial tiles take the general path, one per
-// wavefront. Phases and TAB as for the single kernel.
+// wavefront. Phases and TAB as for the single kernel. Both the table and the
+// direct variants run at four waves per SIMD (the direct one spills a few
+// registers outside its tile loop, and its LDS still fits four blocks per
+// CU): on the 13B list at G = 32 that is about 1 % faster than three waves.
 template <int FM, int FV, bool TAB, int LG>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAB ? 4 : 3, TAB ? 4 : 3))) void step_multi_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void step_multi_kernel(
     const TensorRef* __restrict__ ts, const int64_t* __restrict__ full_begin, const int32_t* __restrict__ partial,
     int count, int n_partial, StepConsts c, int phases) {
     __shared__ typename StepLds<TAB>::Tables ct;
