@@ -958,28 +958,40 @@ __device__ __forceinline__ void build_tables(WaveLdsTab& wl, const TabTables& ct
     if (t == 3) {
         const int NEG = e4 ? 16 : 8;
         double* g = reinterpret_cast<double*>(gb);
+        // The constant entries, from high words materialized here (opaque to
+        // the optimizer): held across the tile loop instead, these constants
+        // took eight registers.
+        uint32_t h_nz = 0x80000000u, h_one = 0x3FF00000u, h_mone = 0xBFF00000u, h_nan = 0x7FF80000u,
+                 h_inf = 0x7FF00000u;
+        asm volatile("" : "+v"(h_nz), "+v"(h_one), "+v"(h_mone), "+v"(h_nan), "+v"(h_inf));
+        auto hi_only = [](uint32_t h) { return __builtin_bit_cast(double, (uint64_t)h << 32); };
         g[tsb] = 0.0;
-        g[tsb + NEG] = -0.0;
-        g[tsb + 1] = 1.0;
-        g[tsb + 1 + NEG] = -1.0;
+        g[tsb + NEG] = hi_only(h_nz);
+        g[tsb + 1] = hi_only(h_one);
+        g[tsb + 1 + NEG] = hi_only(h_mone);
         if (e4) {
-            g[te_special<COAT_FMT_E4M3>()] = __builtin_nan("");
+            g[te_special<COAT_FMT_E4M3>()] = hi_only(h_nan);
         } else {
-            g[te_special<COAT_FMT_E5M2>()] = __builtin_inf();
-            g[tsb + kE5TsNan] = __builtin_nan("");
+            g[te_special<COAT_FMT_E5M2>()] = hi_only(h_inf);
+            g[tsb + kE5TsNan] = hi_only(h_nan);
         }
     }
     asm volatile("" ::: "memory");
 }
 
-// b sign(q) (|q| s)^(1/k) + add for byte i of code word w, the product of the
-// group's two table entries fused with the addition.
-__device__ __forceinline__ double table_dequant_fma(uint32_t w, int i, const uint32_t* lut, const GroupTable& g,
-                                                    double add) {
-    const uint32_t e = lut[(w >> (8 * i)) & 0xFFu];
+// The group-table offsets (TE, TS) of byte i of code word w, packed low / high.
+__device__ __forceinline__ uint32_t code_offsets(uint32_t w, int i, const uint32_t* lut) {
+    return lut[(w >> (8 * i)) & 0xFFu];
+}
+// The group's two table entries for a code with table offsets e; their
+// product is b sign(q) (|q| s)^(1/k).
+struct EntryPair {
+    double te, ts;
+};
+__device__ __forceinline__ EntryPair table_entries(uint32_t e, const GroupTable& g) {
     const char* base = reinterpret_cast<const char*>(&g);
-    return __builtin_fma(*reinterpret_cast<const double*>(base + (e & 0xFFFFu)),
-                         *reinterpret_cast<const double*>(base + (e >> 16)), add);
+    return EntryPair{*reinterpret_cast<const double*>(base + (e & 0xFFFFu)),
+                     *reinterpret_cast<const double*>(base + (e >> 16))};
 }
 
 // One wavefront tile of the step: elements [tile*1024, tile*1024 + 1024) of t,
@@ -1094,9 +1106,20 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
         build_tables<FM, FV>(wl, ct, own_group(in.s0, in.k0), lpg);
         const GroupTable& tm = wl.tbl[(lane / lpg) * 2];
         const GroupTable& tv = wl.tbl[(lane / lpg) * 2 + 1];
+        // Software-pipelined: element i's group-table reads are issued before
+        // the code-table reads of element i + 1, so that waiting for the former
+        // leaves the latter in flight and the two dependent LDS round trips of a
+        // lookup overlap (the pass is otherwise bound by LDS latency; about
+        // 1.5 % off the step on the 13B list).
+        uint32_t em = code_offsets(mq[0], 0, ct.lut[0]), ev = code_offsets(vq[0], 0, ct.lut[1]);
         element_pass([&](int i, double cg, double cg2, double& m1, double& v1) {
-            m1 = table_dequant_fma(mq[i >> 2], i & 3, ct.lut[0], tm, cg);
-            v1 = table_dequant_fma(vq[i >> 2], i & 3, ct.lut[1], tv, cg2);
+            const EntryPair xm_ = table_entries(em, tm), xv_ = table_entries(ev, tv);
+            if (i + 1 < kLaneElems) {
+                em = code_offsets(mq[(i + 1) >> 2], (i + 1) & 3, ct.lut[0]);
+                ev = code_offsets(vq[(i + 1) >> 2], (i + 1) & 3, ct.lut[1]);
+            }
+            m1 = __builtin_fma(xm_.te, xm_.ts, cg);
+            v1 = __builtin_fma(xv_.te, xv_.ts, cg2);
         });
         asm volatile("" ::: "memory");  // the park area reuses the tables' LDS
     } else {
