@@ -7,12 +7,16 @@ resident in HBM (about 133 GB). One step = one multi-tensor launch over the
 whole list. Prints one JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama13b]
-                  [--no-cpu-baseline] [--copy-calibration]
+                  [--no-cpu-baseline] [--copy-calibration] [--sweep | --act | --codec]
 
 With --sweep it instead times the step and measures the state codec's
 quantization error for every group size in {32, 64, 128, 256}, format pair
 {E4M3/E4M3, E4M3/E5M2} and expansion on/off, on the same parameter list:
 one JSON line per variant on stdout, a markdown table on stderr.
+
+With --codec it times the FP8 state codec (quantize fp32 moments to codes,
+scales and exponents, and dequantize them back; groups of 32 and 128, m in
+E4M3 and v in E5M2) on 2^30 values: one JSON line per launch kind.
 
 With --act it times the FP8 activation codec (per tensor and per group of 128,
 E4M3 and E5M2) on a 16384 x 13824 bf16 activation matrix (the input of
@@ -206,6 +210,52 @@ def act_bench(args) -> int:
     return 0
 
 
+def codec_bench(args) -> int:
+    """Throughput of the state codec's entry points (quantize fp32 moments to
+    (q, s, k), dequantize back) on 2^30 first- and second-moment-shaped values
+    resident in HBM."""
+    import torch
+
+    import fp8_optimizer_state_amd as coat
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    coat.lib()
+    n = 1 << 30
+    stream = torch.cuda.current_stream()
+    for G in (32, 128):
+        m, v = synth.prior_moments(n, G, 17, 0, device=dev)
+        q = torch.empty(n, dtype=torch.uint8, device=dev)
+        s = torch.empty(coat.ngroups(n, G), dtype=torch.float64, device=dev)
+        k = torch.empty(coat.ngroups(n, G), dtype=torch.float32, device=dev)
+        back = torch.empty(n, dtype=torch.float32, device=dev)
+        for moment, x, fmt, fname in (("m", m, coat.FMT_E4M3, "E4M3"), ("v", v, coat.FMT_E5M2, "E5M2")):
+            bpe = 4.0 + 1.0 + 12.0 / G
+            ops = (("quantize", lambda: coat.quantize(x, q, s, k, group=G, fmt=fmt)),
+                   ("dequantize", lambda: coat.dequantize(q, s, k, back, group=G, fmt=fmt)))
+            for name, fn in ops:
+                for _ in range(args.warmup):
+                    fn()
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                ev0.record(stream)
+                for _ in range(args.steps):
+                    fn()
+                ev1.record(stream)
+                torch.cuda.synchronize()
+                ms = ev0.elapsed_time(ev1) / args.steps
+                gbps = bpe * n / (ms * 1e-3) / 1e9
+                row = {"state_codec": name, "moment": moment, "group": G, "fmt": fname, "n": n, "ms": ms,
+                       "elements_per_s": n / (ms * 1e-3), "bytes_per_element": bpe, "achieved_GBps": gbps,
+                       "frac_of_8TBps": gbps / PEAK_HBM_GBPS}
+                print(json.dumps(row), flush=True)
+                log(f"state codec {name} {moment} G={G} {fname}: {ms:.3f} ms, {gbps:.0f} GB/s")
+        del m, v, q, s, k, back
+        torch.cuda.empty_cache()
+    return 0
+
+
 def cpu_baseline(wl, per_tensor: int = 229376) -> dict:
     """The oracle, single-threaded, on a bounded sample of the workload: the
     first `per_tensor` elements of every tensor (about 65M params for the
@@ -264,6 +314,8 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="time and measure the codec error of every group size / format / expansion variant")
     ap.add_argument("--act", action="store_true", help="time the FP8 activation codec instead of the step")
+    ap.add_argument("--codec", action="store_true",
+                    help="time the FP8 state codec (quantize / dequantize of moments) instead of the step")
     args = ap.parse_args()
     if args.steps < 1 or args.warmup < 0:
         print("bench.py needs --steps >= 1 and --warmup >= 0", file=sys.stderr)
@@ -277,6 +329,8 @@ def main() -> int:
         return sweep(args)
     if args.act:
         return act_bench(args)
+    if args.codec:
+        return codec_bench(args)
 
     import torch
 
