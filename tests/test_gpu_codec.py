@@ -105,8 +105,9 @@ def test_quantize_parity(coat, fmt, G, n):
 
 
 @pytest.mark.parametrize("fmt", [E4, E5])
-@pytest.mark.parametrize("G", [32, 128])
+@pytest.mark.parametrize("G", [32, 128, 256, 1024])
 def test_dequantize_parity(coat, fmt, G):
+    # whole tiles (the table path for groups of 128 and more) and a ragged last tile
     n = 1024 * 50 + 77
     x = page_like(n, G, "m", seed=5)
     q, s, k = oracle.quantize(x.astype(np.float64), G, fmt)
@@ -118,6 +119,41 @@ def test_dequantize_parity(coat, fmt, G):
     want = oracle.dequantize(q, s, k, G, fmt)
     # fp32 output of an fp64 value: one rounding, so within one fp32 ulp of the oracle
     assert np.all(np.abs(got - want) <= np.spacing(np.abs(want).astype(np.float32)).astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+@pytest.mark.parametrize("G", [128, 1024])
+def test_dequantize_every_code_and_special_groups(coat, fmt, G):
+    """Every code under stored states of the kinds the quantizer and the step
+    produce: expanded (k > 1), k = 1, k < 1, an all-zero group (s = 0 with
+    signed-zero and NaN codes) and a poisoned group (s = NaN, every code NaN).
+    NaN results must match in place."""
+    rng = np.random.default_rng(9)
+    ng = 40
+    n = ng * G + 300  # whole tiles and a ragged last tile
+    q = rng.integers(0, 256, n, dtype=np.uint8)
+    q[:256] = np.arange(256, dtype=np.uint8)
+    ngr = (n + G - 1) // G
+    s = 10.0 ** rng.uniform(-40.0, -5.0, ngr)
+    k = rng.uniform(0.7, 10.0, ngr).astype(np.float32)
+    k[1::5] = 1.0
+    s[2] = 0.0
+    q[2 * G:3 * G] = rng.choice(np.array([0x00, 0x80, 0x7F, 0xFF], dtype=np.uint8), G)
+    s[3] = np.nan
+    k[3] = 1.0
+    q[3 * G:4 * G] = 0x7F
+    log(f"test_dequantize_every_code_and_special_groups fmt={fmt} G={G}")
+    X = torch.empty(n, dtype=torch.float32, device="cuda")
+    coat.dequantize(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda(), torch.from_numpy(k).cuda(),
+                    X, group=G, fmt=fmt)
+    got = X.cpu().numpy().astype(np.float64)
+    want = oracle.dequantize(q, s, k, G, fmt)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    fin = ~np.isnan(want)
+    want32 = want[fin].astype(np.float32).astype(np.float64)
+    ok = (got[fin] == want32) | (np.abs(got[fin] - want[fin]) <= np.spacing(np.abs(want[fin]).astype(np.float32)))
+    assert ok.all(), np.flatnonzero(~ok)[:10]
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(want[fin]))
 
 
 @pytest.mark.parametrize("fmt", [E4, E5])
