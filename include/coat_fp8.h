@@ -82,6 +82,10 @@ enum {
  *   v_q,v_s,v_k  second-moment state, same shapes, in/out
  *   fmt_m/fmt_v  COAT_FMT_E4M3 or COAT_FMT_E5M2, optionally | COAT_FMT_NO_EXPAND
  *   step         t >= 1, the step being taken
+ * The stored moments are states written by coat_fp8_quantize or by an earlier
+ * step (an all-zero group stores s = 0 with signed-zero codes, a poisoned
+ * group s = NaN with NaN codes). For states neither writes (an Inf code under
+ * a zero or NaN scale, a scale of +Inf) the result is unspecified.
  */
 int coat_fp8_adamw_step(float* params, uint16_t* params_bf16, const uint16_t* grads,
                         uint8_t* m_q, double* m_s, float* m_k,
