@@ -103,9 +103,12 @@ __device__ __forceinline__ FmtRT fmt_rt() {
 // ------------------------------------------------------------------ cross-lane
 
 // Value of lane (lane ^ 1), (lane ^ 2), ... via DPP within a row of 16.
+// Every pattern used here reads a valid lane of the same row with all rows
+// and banks enabled, so no lane keeps its old value: the move has no "old"
+// operand (an update_dpp with old = 0 costs a v_mov per move to set it).
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ double dpp64(double v) {
