@@ -226,20 +226,22 @@ struct ExpJob {
     int32_t te;  // 1: a TE entry (A = a, times the decay b); 0: a TS entry (and its negative)
 };
 struct ProdJob {
-    uint8_t src, pow, dst, neg;
+    uint8_t src, mul, dst, neg;
 };
+constexpr int kExpJobs = 8;    // per moment: 2 per builder lane
+constexpr int kProdJobs = 32;  // per moment: 8 per builder lane
 struct TableJobs {
-    ExpJob e[12];
-    ProdJob p[28];
+    ExpJob e[kExpJobs];
+    ProdJob p[kProdJobs];  // mul: an entry index (a power of 2^r or a TS entry)
 };
-// One builder lane's share, in the form the builder consumes: three entries
-// fm 2^(fa a + r x) written to `slot` and negated to `nslot`, then seven
+// One builder lane's share, in the form the builder consumes: two entries
+// fm 2^(fa a + r x) written to `slot` and negated to `nslot`, then eight
 // products table[src] * table[mul] written to `dst` and negated to `ndst`
 // (offsets in bytes; the trash slot where no negative is wanted).
 struct LaneJob {
-    double xh[3], xl[3], fa[3], fm[3];
-    uint32_t slot[3], nslot[3];
-    uint32_t src[7], mul[7], dst[7], ndst[7];
+    double xh[2], xl[2], fa[2], fm[2];
+    uint32_t slot[2], nslot[2];
+    uint32_t src[8], mul[8], dst[8], ndst[8];
 };
 struct alignas(16) LqEntry {
     double lq;
@@ -332,10 +334,10 @@ __device__ double lqm_entry(int c) {
 //   E4M3: TE[0..15], NaN at 16 (its NaN code); TS[0..31] at 17..48;
 //   E5M2: TE[0..30], Inf at 31 (e = 31); TS[0..15] at 32..47, NaN at 48
 //         (its NaN codes);
-//   both: the powers (2^r)^0..3 at 49..52, a trash slot at 53.
-constexpr int kGroupTableN = 54;
+//   both: the powers (2^r)^0..7 at 49..56, a trash slot at 57.
+constexpr int kGroupTableN = 58;
 constexpr int kPowBase = 49;
-constexpr int kTrash = 53;
+constexpr int kTrash = 57;
 struct GroupTable {
     double v[kGroupTableN];
 };
@@ -359,31 +361,34 @@ __device__ uint32_t lut_entry(int code) {
     return te_off | (ts_off << 16);
 }
 
-// The work of building one moment's table, split over four lanes: 12 entries
+// The work of building one moment's table, split over four lanes: 8 entries
 // evaluated as 2^(A + r x) (x = log2 i for TS[i], A = 0; x = max(e,1) - BIAS
-// - MB - log2 fpmax for TE[e], A = a), 3 per lane, then up to 28 products
-// table[dst] = table[src] * (2^r)^pow, 7 per lane. Entries:
-//   E4M3: TS[i], i in {2,3,5,7,9,11,13,15}; TE anchors {0,4,8,12};
-//   E5M2: TS[i], i in {2,3,5,7}; TE anchors {0,4,...,28}.
-// TS[2i] = TS[i] 2^r and TE[e + j] = TE[e] 2^(r j) for e >= 1 (TE[0] = TE[1],
-// so from the anchor 0 the powers start at 0). Unused product slots write a
-// trash entry that no code reads.
+// - MB - log2 fpmax for TE[e], A = a), 2 per lane, then up to 32 products
+// table[dst] = table[src] * table[mul], 8 per lane. Entries:
+//   E4M3: TS[i], i in {2,3,5,7,11,13}; TE anchors {0,8};
+//   E5M2: TS[i], i in {2,3,5,7}; TE anchors {0,8,16,24}.
+// Products: TS[2i] = TS[i] 2^r, TS[9] = TS[3]^2, TS[15] = TS[3] TS[5], and
+// TE[e + j] = TE[e] 2^(r j) for e >= 1, j < 8 (TE[0] = TE[1], so from the
+// anchor 0 the powers start at 0). They read only the evaluated entries and
+// the powers, never each other. Unused product slots write a trash entry that
+// no code reads.
 template <int F>
 __device__ void table_jobs(TableJobs& j, int tid) {
     using T = Fmt<F>;
     constexpr bool E4 = F == COAT_FMT_E4M3;
-    constexpr int NTS = E4 ? 8 : 4;
+    constexpr int NTS = E4 ? 6 : 4;
     constexpr int TSB = ts_base<F>();
-    if (tid < 12) {
+    constexpr int NTE = E4 ? 16 : 31;  // TE entries (E5M2: 31 is the Inf entry)
+    if (tid < kExpJobs) {
         ExpJob& e = j.e[tid];
         if (tid < NTS) {
-            const int ts[8] = {2, 3, 5, 7, 9, 11, 13, 15};
+            const int ts[6] = {2, 3, 5, 7, 11, 13};
             const int i = ts[tid];
             e.xh = log2_full_dd((double)i, e.xl);
             e.slot = TSB + i;
             e.te = 0;
         } else {
-            const int a = 4 * (tid - NTS);
+            const int a = 8 * (tid - NTS);
             const double x = (double)((a > 0 ? a : 1) - T::BIAS - T::MB);
             const double h = x - T::LOG2_FPMAX;
             const double bb = h - x;
@@ -392,18 +397,21 @@ __device__ void table_jobs(TableJobs& j, int tid) {
             e.slot = a;
             e.te = 1;
         }
-    } else if (tid < 12 + 28) {
-        const int q = tid - 12;
+    } else if (tid < kExpJobs + kProdJobs) {
+        const int q = tid - kExpJobs;
         ProdJob pj{0, 0, (uint8_t)kTrash, 0};
-        // TS products first, then the TE chains
-        const int ts_src[6] = {2, 3, 2, 5, 3, 7}, ts_pow[6] = {1, 1, 2, 1, 2, 1}, ts_dst[6] = {4, 6, 8, 10, 12, 14};
-        const int nts = E4 ? 6 : 2;
-        const int nte = (E4 ? 4 : 8) * 3;
+        // TS products first (src, mul, dst), then the TE chains
+        const int ts_src[8] = {2, 3, 2, 5, 3, 7, 3, 3};
+        const int ts_mul[8] = {kPowBase + 1, kPowBase + 1, kPowBase + 2, kPowBase + 1, kPowBase + 2, kPowBase + 1,
+                               TSB + 3, TSB + 5};
+        const int ts_dst[8] = {4, 6, 8, 10, 12, 14, 9, 15};
+        const int nts = E4 ? 8 : 2;
         if (q < nts) {
-            pj = ProdJob{(uint8_t)(TSB + ts_src[q]), (uint8_t)ts_pow[q], (uint8_t)(TSB + ts_dst[q]), 1};
-        } else if (q < nts + nte) {
-            const int r = q - nts, a = 4 * (r / 3), jj = 1 + r % 3;
-            pj = ProdJob{(uint8_t)a, (uint8_t)(a == 0 ? jj - 1 : jj), (uint8_t)(a + jj), 0};
+            pj = ProdJob{(uint8_t)(TSB + ts_src[q]), (uint8_t)ts_mul[q], (uint8_t)(TSB + ts_dst[q]), 1};
+        } else {
+            const int r = q - nts, a = 8 * (r / 7), jj = 1 + r % 7;
+            if (a + jj < NTE)
+                pj = ProdJob{(uint8_t)a, (uint8_t)(kPowBase + (a == 0 ? jj - 1 : jj)), (uint8_t)(a + jj), 0};
         }
         j.p[q] = pj;
     }
@@ -444,8 +452,8 @@ __device__ __forceinline__ void fill_tab_tables(TabTables& ct, TabScratch& scrat
         const uint32_t NEG = e4 ? 16 : 8;
         const TableJobs& J = scratch.jobs[mu];
         LaneJob& L = ct.lj[threadIdx.x];
-        for (int q = 0; q < 3; ++q) {
-            const ExpJob& e = J.e[3 * t + q];
+        for (int q = 0; q < 2; ++q) {
+            const ExpJob& e = J.e[2 * t + q];
             L.xh[q] = e.xh;
             L.xl[q] = e.xl;
             L.fa[q] = e.te ? 1.0 : 0.0;
@@ -453,10 +461,10 @@ __device__ __forceinline__ void fill_tab_tables(TabTables& ct, TabScratch& scrat
             L.slot[q] = 8u * (uint32_t)e.slot;
             L.nslot[q] = 8u * (e.te ? (uint32_t)kTrash : (uint32_t)e.slot + NEG);
         }
-        for (int q = 0; q < 7; ++q) {
-            const ProdJob& pj = J.p[7 * t + q];
+        for (int q = 0; q < 8; ++q) {
+            const ProdJob& pj = J.p[8 * t + q];
             L.src[q] = 8u * pj.src;
-            L.mul[q] = 8u * (kPowBase + pj.pow);
+            L.mul[q] = 8u * pj.mul;
             L.dst[q] = 8u * pj.dst;
             L.ndst[q] = 8u * (pj.neg ? (uint32_t)pj.dst + NEG : (uint32_t)kTrash);
         }
@@ -916,7 +924,8 @@ __device__ __forceinline__ void fma_dd(double ah, double al, double rh, double r
 // Builds the group tables of this tile (groups of 8 lanes or more): lanes
 // 0..3 of each group build the first moment's table, lanes 4..7 the second's,
 // each taking its LaneJob. Every entry is a correctly rounded 2^(A + r x)
-// with a double-double exponent, or a product of at most three such values.
+// with a double-double exponent, or a product of such values with at most
+// five roundings (TE[15] = TE[8] (2^r)^7, (2^r)^7 = (2^r)^4 (2^r)^3).
 template <int FM, int FV>
 __device__ __forceinline__ void build_tables(WaveLdsTab& wl, const TabTables& ct, const OldGroup& og, int lpg) {
     // opaque, so that the lane's job parameters are derived in each tile
@@ -933,7 +942,7 @@ __device__ __forceinline__ void build_tables(WaveLdsTab& wl, const TabTables& ct
     const double a = og.a, a_lo = og.a_lo, r = og.r, r_lo = og.r_lo;
     const LaneJob& J = ct.lj[l];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
+    for (int q = 0; q < 2; ++q) {
         double h, lo;
         fma_dd(J.fa[q] * a, J.fa[q] * a_lo, r, r_lo, J.xh[q], J.xl[q], h, lo);
         const double v = J.fm[q] * exp2_dd(h, lo);
@@ -943,14 +952,19 @@ __device__ __forceinline__ void build_tables(WaveLdsTab& wl, const TabTables& ct
     asm volatile("" ::: "memory");
     if (t == 0) {
         const double P = at(8u * (tsb + 2));
+        const double P2 = P * P, P3 = P2 * P, P4 = P2 * P2;
         at(8u * kPowBase) = 1.0;
         at(8u * (kPowBase + 1)) = P;
-        at(8u * (kPowBase + 2)) = P * P;
-        at(8u * (kPowBase + 3)) = P * P * P;
+        at(8u * (kPowBase + 2)) = P2;
+        at(8u * (kPowBase + 3)) = P3;
+        at(8u * (kPowBase + 4)) = P4;
+        at(8u * (kPowBase + 5)) = P4 * P;
+        at(8u * (kPowBase + 6)) = P4 * P2;
+        at(8u * (kPowBase + 7)) = P4 * P3;
     }
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int q = 0; q < 7; ++q) {
+    for (int q = 0; q < 8; ++q) {
         const double v = at(J.src[q]) * at(J.mul[q]);
         at(J.dst[q]) = v;
         at(J.ndst[q]) = -v;
