@@ -57,8 +57,7 @@ def lib() -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                           "or python -m fp8_optimizer_state_amd._build")
+        raise RuntimeError(f"{LIB_PATH} is not built; run python -m fp8_optimizer_state_amd._build")
     L = ctypes.CDLL(LIB_PATH)
     P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     hyper = [f32, f32, f32, f32, f32, i64]
