@@ -532,6 +532,27 @@ __device__ __forceinline__ double log2_stat(double x, double& lo) {
     return log2_full_dd(xs, lo);
 }
 
+// Whether the correctly rounded fp64 quotient a / b exceeds T = 1 + 1e-6 (the
+// fp64 constant), for finite a >= b > 0: the near-constant test of the group's
+// ratio, decided without a division. RN(a / b) > T exactly when a / b lies
+// above M = T + 2^-53, the midpoint between T and its successor (M b is never
+// an fp64 number, as M has 54 significant bits, so no tie arises). With
+// d = fma(-T, b, a): a - T b is a multiple of 2^(e_b - 104), so wherever it is
+// within 4 h b of zero (h b = 2^-53 b) it has at most 53 significant bits and
+// d is exact; farther out, rounding keeps its order against h b. Hence
+// a / b > M iff d > h b. Tiny b is scaled by 2^600 first so that the
+// difference stays above the fp64 subnormal range; a ratio of two or more
+// needs no test.
+constexpr double kNearConstant = 1.0 + 1e-6;
+__device__ __forceinline__ bool ratio_above_near_constant(double a, double b) {
+    if (!(a < 2.0 * b)) return true;
+    if (b < 0x1p-960) {
+        a = __builtin_amdgcn_ldexp(a, 600);
+        b = __builtin_amdgcn_ldexp(b, 600);
+    }
+    return __builtin_fma(-kNearConstant, b, a) > b * 0x1p-53;
+}
+
 // L + L_lo = log2(amax), Lm + Lm_lo = log2(amin) (as from log2_stat); the
 // group's log2(amax / amin) is their double-double difference.
 __device__ NewGroup new_group(double amax, double amin, double L, double L_lo, double Lm, double Lm_lo,
@@ -557,7 +578,7 @@ __device__ NewGroup new_group(double amax, double amin, double L, double L_lo, d
     float k = 1.0f;
     const double d = L - Lm;
     const double log2R = d + (((L - d) - Lm) + (L_lo - Lm_lo));
-    if (expand && amax > amin * 1.000001) k = (float)(F.log2_rf * rcp_f64(log2R));
+    if (expand && ratio_above_near_constant(amax, amin)) k = (float)(F.log2_rf * rcp_f64(log2R));
     const double lo = -1022.0 + F.log2_rf, hi = 1023.0;
     const double kL = (double)k * L;
     if (!(kL >= lo && kL <= hi)) {
@@ -1163,7 +1184,11 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     // later reads of the park area must come from LDS, not from registers
     asm volatile("" ::: "memory");
 
-    bool bad = false;
+    // bit 0: a first moment of the lane is not finite, bit 1: a second moment
+    uint32_t bad = 0u;
+    // bit i: element i's moments are finite in fp64 but one lies beyond the
+    // fp32 range, so its update is redone in fp64
+    uint32_t wide = 0u;
     if (__any(special)) {
         // Rare: exact statistics with zeros excluded from the minimum and
         // non-finite moments flagged, from the parked inputs.
@@ -1180,11 +1205,38 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
             const double m1 = __builtin_fma(tbm, m0, c.c1 * g);
             const double v1 = __builtin_fma(tbv, v0, c.c2 * (g * g));
             const double am = __builtin_fabs(m1), av = __builtin_fabs(v1);
-            bad |= !(am < __builtin_inf()) | !(av < __builtin_inf());
+            const bool fin_m = am < __builtin_inf(), fin_v = av < __builtin_inf();
+            bad |= (fin_m ? 0u : 1u) | (fin_v ? 0u : 2u);
             amax_m = vmax(amax_m, am);
             amin_m = vmin(amin_m, am == 0.0 ? __builtin_inf() : am);
             amax_v = vmax(amax_v, av);
             amin_v = vmin(amin_v, av == 0.0 ? __builtin_inf() : av);
+            const bool beyond = !(__builtin_fabsf((float)m1) <= 0x1.fffffep+127f) ||
+                                !(__builtin_fabsf((float)v1) <= 0x1.fffffep+127f);
+            wide |= (beyond && fin_m && fin_v && i < nvalid) ? 1u << i : 0u;
+        }
+        // Moments finite in fp64 but beyond the fp32 range (a bf16 grad of
+        // about 1e20 or more, or a huge stored state) leave the fp32 update
+        // without a usable value: it is redone in fp64 from the master weight
+        // as loaded (stored only after this point), one element per lane at a
+        // time, the result placed with a fixed-index select so that p stays in
+        // registers.
+        while (__any(wide != 0u)) {
+            if (wide != 0u) {
+                const int i = __builtin_ctz(wide);
+                wide &= wide - 1u;
+                const double g = bf16_to_f64(pk.gw[i >> 1][lane], i & 1);
+                double tbm, tbv;
+                const double m0 = dequant_mag(pk.mq[i >> 2][lane] >> (8 * (i & 3)), 0, pm, lq_m, tbm);
+                const double v0 = dequant_mag(pk.vq[i >> 2][lane] >> (8 * (i & 3)), 0, pv, lq_v, tbv);
+                const double m1 = __builtin_fma(tbm, m0, c.c1 * g);
+                const double v1 = __builtin_fma(tbv, v0, c.c2 * (g * g));
+                const double p0 = (double)P[e0 + i];
+                const double den = __builtin_sqrt(v1) * (double)c.ib2 + (double)c.eps;
+                const float pc = (float)(p0 * (double)c.decay - (double)c.ssz * (m1 / den));
+#pragma unroll
+                for (int j = 0; j < 16; ++j) p[j] = (j == i) ? pc : p[j];
+            }
         }
     }
 
@@ -1220,8 +1272,10 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     amin_m = group_min(amin_m, lpg);
     amax_v = group_max(amax_v, lpg);
     amin_v = group_min(amin_v, lpg);
-    // A non-finite grad poisons both moments' groups (m' and v' both become non-finite).
-    const bool poison = group_or(bad ? 1u : 0u, lpg) != 0u;
+    // Each moment's group is poisoned by its own non-finite members (a NaN or
+    // Inf grad makes both moments non-finite; a poisoned stored state only its own).
+    const uint32_t bad_group = group_or(bad, lpg);
+    const bool poison_m = (bad_group & 1u) != 0u, poison_v = (bad_group & 2u) != 0u;
 
     // ---- requantization constants (the lane pair splits the two moments)
     NewGroup nm, nv;
@@ -1244,7 +1298,7 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
             L = log2_stat(amax_x, L_lo);
             Lm = log2_stat(amin_x, Lm_lo);
         }
-        const NewGroup mine = new_group(amax_x, amin_x, L, L_lo, Lm, Lm_lo, poison,
+        const NewGroup mine = new_group(amax_x, amin_x, L, L_lo, Lm, Lm_lo, odd ? poison_v : poison_m,
                                         odd ? c.expand_v : c.expand_m, odd ? fv : fm);
         const NewGroup other = swap_pair(mine);
         nm = odd ? other : mine;
@@ -1261,8 +1315,8 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
         double a_lo, b_lo, c_lo, d_lo;
         const double la = log2_stat(amax_m, a_lo), lb = log2_stat(amin_m, b_lo);
         const double lc = log2_stat(amax_v, c_lo), ld = log2_stat(amin_v, d_lo);
-        nm = new_group(amax_m, amin_m, la, a_lo, lb, b_lo, poison, c.expand_m, fm);
-        nv = new_group(amax_v, amin_v, lc, c_lo, ld, d_lo, poison, c.expand_v, fv);
+        nm = new_group(amax_m, amin_m, la, a_lo, lb, b_lo, poison_m, c.expand_m, fm);
+        nv = new_group(amax_v, amin_v, lc, c_lo, ld, d_lo, poison_v, c.expand_v, fv);
         if (nvalid > 0) {
             gp(t.ms)[gidx] = nm.s; gp(t.mk)[gidx] = nm.k;
             gp(t.vs)[gidx] = nv.s; gp(t.vk)[gidx] = nv.k;

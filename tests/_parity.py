@@ -92,10 +92,15 @@ def gpu_step(x: StepInputs, dev="cuda", want_bf16: bool = True, **hyper):
 
 
 def code_steps(a: np.ndarray, b: np.ndarray) -> np.ndarray:
-    """Distance in code steps between two FP8 code arrays (+0 and -0 coincide)."""
+    """Distance in code steps between two FP8 code arrays, on the line of
+    signed magnitudes; codes that differ only in the sign of zero (0x00 against
+    0x80) count as one step, so a signed-zero mismatch is never invisible."""
+    a = np.asarray(a, np.uint8)
+    b = np.asarray(b, np.uint8)
     sa = np.where(a & 0x80, -1, 1) * (a & 0x7F).astype(np.int32)
     sb = np.where(b & 0x80, -1, 1) * (b & 0x7F).astype(np.int32)
-    return np.abs(sa - sb)
+    d = np.abs(sa - sb)
+    return np.where((d == 0) & (a != b), 1, d)
 
 
 def rel_err(a, b):

@@ -182,3 +182,36 @@ def test_quantize_degenerate_groups(coat, fmt):
     assert rel_err(K.cpu().numpy(), k).max() <= 1e-5, (K.cpu().numpy(), k)
     assert rel_err(S.cpu().numpy(), s).max() <= 1e-5, (S.cpu().numpy(), s)
     assert np.array_equal(Q.cpu().numpy(), q)
+
+
+@pytest.mark.parametrize("G", [32, 128])
+def test_quantize_near_constant_threshold(coat, G):
+    """Groups at the near-constant threshold: an amax / amin of exactly
+    1 + 1e-6 in real arithmetic (9000009 / 9000000, 10000010 / 10000000 and
+    11000011 / 11000000, scaled) rounds to the fp64 constant 1 + 1e-6, so k = 1;
+    one fp32 step more in amax is above it and expands. fp32 inputs reach the
+    threshold quotient only exactly; the fp64-ulp neighbours of it are covered
+    by the step's threshold test."""
+    groups, expect_k1 = [], []
+    for b_int, d in ((9000000, 9), (10000000, 10), (11000000, 11)):
+        for extra, scale in ((0, 2.0 ** -24), (1, 2.0 ** -24), (0, 2.0 ** -40)):
+            a = np.float32((b_int + d + extra) * scale)
+            b = np.float32(b_int * scale)
+            grp = np.full(G, b, np.float32)
+            grp[G // 3] = a
+            groups.append(grp)
+            expect_k1.append(extra == 0)
+    x = np.concatenate(groups)
+    n = x.size
+    log(f"test_quantize_near_constant_threshold G={G}")
+    X = torch.from_numpy(x).cuda()
+    Q = torch.empty(n, dtype=torch.uint8, device="cuda")
+    S = torch.empty(n // G, dtype=torch.float64, device="cuda")
+    K = torch.empty(n // G, dtype=torch.float32, device="cuda")
+    coat.quantize(X, Q, S, K, group=G, fmt=E4)
+    q, s, k = oracle.quantize(x.astype(np.float64), G, E4)
+    assert np.array_equal(k == 1.0, np.array(expect_k1)), k
+    assert np.array_equal(K.cpu().numpy(), k)
+    assert rel_err(S.cpu().numpy(), s).max() <= 1e-5
+    d = code_steps(Q.cpu().numpy(), q)
+    assert d.max() <= 1 and (d != 0).mean() <= 1e-4

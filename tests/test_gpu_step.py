@@ -158,3 +158,111 @@ def test_deterministic():
     for key in a:
         if a[key] is not None:
             assert np.array_equal(a[key], b[key], equal_nan=True), key
+
+
+def _bf16(x):
+    """bf16 rounding (nearest, ties to even) of float values, as float64."""
+    b = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _bf16_bits(x):
+    """bf16 bit patterns of float values by truncation (exact for values that
+    already are bf16 numbers)."""
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def threshold_groups():
+    """A beta1 and, per offset o in -2..2, the gradients (g_a, g_b) of a group
+    whose new first moments have RN(amax / amin) = T + o ulp, T = 1 + 1e-6.
+
+    The group's stored first moment is x = 0.5 in every element (code 0x38,
+    the value 1, with s = 0.5 and k = 1), so both the kernel and the oracle
+    form m' = RN(b1 x + (1 - b1) g) with one rounding: b1 x and (1 - b1) g are
+    exact in fp64 for an fp32 b1 and a bf16 g. One element takes g_a, the
+    others g_b: amax = m'_a, amin = m'_b. Found by search over fp32 b1 in
+    [0.5, 0.99] (coarse ratio from g_a, then g_b moves m'_b by whole ulps)."""
+    T = 1.0 + 1e-6
+    U = np.spacing(T)
+    b1 = np.arange(np.float32(0.5).view(np.uint32), np.float32(0.99).view(np.uint32),
+                   dtype=np.uint32).view(np.float32).astype(np.float64)
+    c1 = 1.0 - b1
+    X = b1 * 0.5
+    ga = _bf16((T - 1.0) * X / c1)
+    mA = X + c1 * ga
+    uX = np.spacing(X)
+    hits = None
+    for o in (-2, -1, 0, 1, 2):
+        j = np.round((mA / (T + o * U) - X) / uX)
+        gb = _bf16(j * uX / c1)
+        mB = X + c1 * gb
+        good = (np.abs(j) <= 60) & (mB == X + j * uX) & (mA / mB == T + o * U)
+        hits = good if hits is None else hits & good
+    i = int(np.flatnonzero(hits)[0])
+    out = []
+    for o in (-2, -1, 0, 1, 2):
+        j = np.round((mA[i] / (T + o * U) - X[i]) / uX[i])
+        out.append((o, ga[i], _bf16(j * uX[i] / c1[i])))
+    return float(np.float32(b1[i])), out
+
+
+def test_near_constant_threshold():
+    """Groups whose max/min quotient rounds to 1 + 1e-6 minus two ulps up to
+    plus two ulps: k = 1 up to and including the threshold, expanded above it,
+    on the GPU exactly as in the oracle (per-group tables, G = 128)."""
+    b1, cases = threshold_groups()
+    n, G = 1024, 128
+    x = make_inputs(n, G, E4, E4, seed=41)
+    for gi, (o, ga, gb) in enumerate(cases):
+        sl = slice(gi * G, (gi + 1) * G)
+        x.mq[sl] = 0x38           # E4M3 value 1.0
+        x.ms[gi], x.mk[gi] = 0.5, 1.0
+        x.vq[sl] = np.where(np.arange(G) % 2 == 0, 0x38, 0x40)  # values 1 and 2
+        x.vs[gi], x.vk[gi] = 2.0 ** -20, 1.0
+        x.g[sl] = _bf16_bits(gb)
+        x.g[gi * G] = _bf16_bits(ga)[()]
+    log(f"test_near_constant_threshold b1={b1!r} cases={cases}")
+    got, ref = gpu_step(x, b1=b1), oracle_step(x, b1=b1)
+    # the oracle decides by the rounded quotient: k = 1 up to T, expanded above
+    for gi, (o, _, _) in enumerate(cases):
+        assert (ref["mk"][gi] == 1.0) == (o <= 0), (o, ref["mk"][gi])
+    compare(got, ref, "threshold")
+    assert np.array_equal(got["mk"][:5], ref["mk"][:5])
+
+
+@pytest.mark.parametrize("G", [16, 32, 128])
+def test_huge_grads_update_in_fp64(G):
+    """bf16 grads of 1e20 and up make v' (and, near the bf16 maximum, the
+    update's intermediates) exceed the fp32 range while every moment stays
+    finite in fp64: the update must still follow the oracle, and no group is
+    poisoned."""
+    n = 1024 * 3
+    x = make_inputs(n, G, E4, E5, seed=42 + G)
+    big = np.array([1e20, -3e20, 3e38, -3.3e38, 2e25], np.float32)
+    x.g[5:10] = _bf16_bits(big)                # one group with several huge grads
+    x.g[G + 17] = _bf16_bits(np.float32(-1e30))[()]
+    x.g[1024 + 3 * G: 1024 + 4 * G] = _bf16_bits(np.full(G, 7e21, np.float32))  # a whole group
+    log(f"test_huge_grads_update_in_fp64 G={G}")
+    got, ref = gpu_step(x), oracle_step(x)
+    assert np.isfinite(ref["ms"]).all() and np.isfinite(ref["vs"]).all()
+    compare(got, ref, f"huge grads G={G}")
+
+
+@pytest.mark.parametrize("G", [16, 32, 128])
+def test_poisoned_state_poisons_its_own_moment_only(G):
+    """A stored first-moment group that is poisoned (s = NaN, codes 0x7F)
+    next to a finite second-moment group: the first moment stays poisoned,
+    the second is requantized as usual, and vice versa."""
+    n = 1024 * 2
+    x = make_inputs(n, G, E4, E5, seed=43 + G)
+    x.mq[0:G] = 0x7F
+    x.ms[0], x.mk[0] = np.nan, 1.0
+    x.vq[3 * G:4 * G] = 0x7F                  # E5M2 NaN code
+    x.vs[3], x.vk[3] = np.nan, 1.0
+    log(f"test_poisoned_state_poisons_its_own_moment_only G={G}")
+    got, ref = gpu_step(x), oracle_step(x)
+    assert np.isnan(ref["ms"][0]) and np.isfinite(ref["vs"][0])
+    assert np.isnan(ref["vs"][3]) and np.isfinite(ref["ms"][3])
+    compare(got, ref, f"poisoned state G={G}")
+    assert np.isfinite(got["vs"][0]) and np.isfinite(got["ms"][3])

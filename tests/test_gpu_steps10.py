@@ -2,17 +2,25 @@
 for both moments, fresh seeded grads every step (t = 10..19).
 
 Checks, on a sample of groups (every tensor's first and last group and every
-997th group): parity with the oracle after every step, each side carrying its
-own state (the full tolerance after the first step; afterwards the two chains
-may part in a few groups, because a k that lands within an fp32 rounding
-boundary of the oracle's changes that group's later states, so later steps
-bound the fraction of groups outside the tolerance); and the drift of the dequantized moments against a dense AdamW
-(fp64 moments, no quantization) started from the same dequantized prior and
-fed the same grads, with expansion and with k forced to 1 (the ablation). The
-article reports that expansion lowers the quantization error of the states
-(section "Solution: dynamic range expansion"); here it must lower the drift.
+997th group):
+  * parity at every step on the same inputs: the oracle takes the step from the
+    GPU's own sampled state after the previous step (the oracle's own state
+    at t = 10) and the same grads, and the GPU's result must match it at the
+    full tolerance (the article recomputes k at every training step, section
+    "Solution: dynamic range expansion", so every step is held to it);
+  * the two chains run side by side, each carrying its own state: where a k
+    lands within an fp32 rounding boundary of the oracle's, that group's later
+    states legitimately differ ("parted" groups), so this is reported and only
+    loosely bounded;
+  * the drift of the dequantized moments against a dense AdamW (fp64 moments,
+    no quantization) started from the same dequantized prior and fed the same
+    grads, with expansion and with k forced to 1 (the ablation). The article
+    reports that expansion lowers the quantization error of the states
+    (section "Solution: dynamic range expansion"); here it must lower the
+    drift.
 """
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -92,6 +100,11 @@ def chain_compare(got, ref, G, label, parted):
     return met
 
 
+def oracle_map(fn, items, threads=16):
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(fn, items))
+
+
 def run(coat, wl, fmt, sample):
     dev = torch.device("cuda")
     G = wl.group
@@ -103,8 +116,10 @@ def run(coat, wl, fmt, sample):
     # dense reference starts from the oracle's dequantized prior
     dense = [dict(p=x["p"].copy(), m=oracle.dequantize(x["mq"], x["ms"], x["mk"], G, fmt & 0xFF),
                   v=oracle.dequantize(x["vq"], x["vs"], x["vk"], G, fmt & 0xFF)) for x in host]
-    ora = [dict(p=x["p"], mq=x["mq"], ms=x["ms"], mk=x["mk"], vq=x["vq"], vs=x["vs"], vk=x["vk"]) for x in host]
-    times = []
+    keys = ("p", "mq", "ms", "mk", "vq", "vs", "vk")
+    ora = [{k: x[k] for k in keys} for x in host]    # the oracle's own chain
+    prev = [{k: x[k] for k in keys} for x in host]   # the GPU's state before the step
+    times, same_input = [], []
     parted = np.zeros(sum(len(x["idx"]) for x in host), dtype=bool)
     for j, step in enumerate(range(10, 10 + wl.steps)):
         # fresh grads for this step, on the device and for the sample on the host
@@ -120,28 +135,36 @@ def run(coat, wl, fmt, sample):
         e1.record()
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
-        new = []
-        for x, o, d in zip(host, ora, dense):
-            r = oracle.adamw_step(o["p"], x["g"], o["mq"], o["ms"], o["mk"], o["vq"], o["vs"], o["vk"],
-                                  G, fmt, fmt, h["lr"], h["b1"], h["b2"], h["eps"], h["wd"], step)
-            new.append(r)
+
+        def oracle_from(state):
+            def one(ix):
+                x, o = ix
+                return oracle.adamw_step(o["p"], x["g"], o["mq"], o["ms"], o["mk"], o["vq"], o["vs"], o["vk"],
+                                         G, fmt, fmt, h["lr"], h["b1"], h["b2"], h["eps"], h["wd"], step)
+            return oracle_map(one, list(zip(host, state)))
+
+        fed = oracle_from(prev)   # same inputs as the GPU's step
+        ora = oracle_from(ora)    # the oracle's own chain
+        for x, d in zip(host, dense):
             d["p"], _, d["m"], d["v"] = oracle.adamw_dense(d["p"], x["g"], d["m"], d["v"], h["lr"], h["b1"],
                                                           h["b2"], h["eps"], h["wd"], step)
-        ora = new
         got = read_sample(st, host, G)
         label = f"{'noexp' if fmt & NOEXP else 'exp'} t={step}"
+        met = compare(concat(got), concat(fed), label + " same inputs")
+        same_input.append(met)
         if j == 0:
-            compare(concat(got), concat(ora), label)
             mark_parted(concat(got), concat(ora), G, parted)
         else:
-            chain_compare(concat(got), concat(ora), G, label, parted)
+            chain_compare(concat(got), concat(ora), G, label + " chains", parted)
+        prev = [{k: d[k] for k in keys} for d in got]
         log(f"  step {step}: {times[-1]:.2f} ms ({wl.n_params / (times[-1] * 1e-3):.3e} params/s)")
     md, vd = dequant_sample_gpu(coat, st, host, G, fmt & 0xFF)
     mref = np.concatenate([d["m"] for d in dense])
     vref = np.concatenate([d["v"] for d in dense])
     del st
     torch.cuda.empty_cache()
-    return dict(times=times, m=groupwise(md, mref, G), v=groupwise(vd, vref, G))
+    return dict(times=times, m=groupwise(md, mref, G), v=groupwise(vd, vref, G), same_input=same_input,
+                parted=int(parted.sum()), groups=int(parted.size))
 
 
 def test_ten_steps_drift_and_ablation(coat):
@@ -151,9 +174,15 @@ def test_ten_steps_drift_and_ablation(coat):
         f"{sum(len(ix) for _, ix in sample) * wl.group} params")
     t0 = time.time()
     exp = run(coat, wl, 0, sample)
-    log(f"  expansion: drift m (global, mean, p99) {exp['m']}, v {exp['v']} ({time.time() - t0:.0f} s)")
+    log(f"  expansion: drift m (global, mean, p99) {exp['m']}, v {exp['v']}, parted chains "
+        f"{exp['parted']} of {exp['groups']} groups ({time.time() - t0:.0f} s)")
     noexp = run(coat, wl, NOEXP, sample)
-    log(f"  k = 1:     drift m (global, mean, p99) {noexp['m']}, v {noexp['v']} ({time.time() - t0:.0f} s)")
+    log(f"  k = 1:     drift m (global, mean, p99) {noexp['m']}, v {noexp['v']}, parted chains "
+        f"{noexp['parted']} of {noexp['groups']} groups ({time.time() - t0:.0f} s)")
+    for name, r in (("expansion", exp), ("k = 1", noexp)):
+        worst = {k: max(m[k] for m in r["same_input"]) for k in ("m_s_rel", "v_s_rel", "m_k_rel", "v_k_rel",
+                                                                 "m_code_frac", "v_code_frac")}
+        log(f"  {name}: same-input parity over t = 10..19, worst {worst}")
     log(f"  median ms/step {np.median(exp['times']):.2f} (expansion), {np.median(noexp['times']):.2f} (k = 1)")
     # expansion keeps the states closer to unquantized AdamW
     assert exp["m"][0] < noexp["m"][0] and exp["v"][0] < noexp["v"][0]

@@ -1,15 +1,29 @@
 """The article's qualitative claims, recomputed with the oracle (CPU).
 
-COAT article (blob.wenxiaobai.com), sections "Solution: dynamic range
+COAT article (blob.wenxiaobai.com), section "Solution: dynamic range
 expansion" and the paragraph after it:
   * expansion cuts the quantization error of the optimizer states;
-  * E4M3 is the better format for the first moment;
+  * E4M3 suits the first moment better than E5M2;
   * for the second moment E4M3 beats E5M2 without expansion, and the two are
     almost the same once expansion is applied.
-The article does not name its error metric; the per-group normwise relative
-error ||x_hat - x|| / ||x|| averaged over groups is the reading under which all
-of its orderings hold, and it is the one asserted here. The element-wise mean
-relative error is reported beside it.
+The article names no error metric. The primary metric here is the plain
+reading of "mean relative quantization error": the element-wise mean of
+|x_hat - x| / |x| over all elements. The per-group normwise error
+||x_hat - x|| / ||x|| averaged over groups is measured beside it. Each claim is
+asserted under the metric where it holds, and where a claim holds under only
+one of them, the other's opposite ordering is asserted too, so that the
+finding itself is pinned (values on page-shaped groups, G = 128, 4000 groups):
+
+  claim                                  element-wise          normwise
+  expansion < k = 1 (m and v, E4M3/E5M2)  holds                 holds
+  m: E4M3 < E5M2 at k = 1                 holds (2.24 / 4.47 %) holds
+  m: E4M3 < E5M2 with expansion           REVERSED (1.95 / 1.53 %)  holds (1.36 / 1.53 %)
+  v: E4M3 < E5M2 at k = 1                 holds                 holds
+  v: E4M3 ~ E5M2 with expansion           within 25 %           within 2 %
+
+Under expansion 16.7 % of the E4M3 first-moment codes are subnormal (6.4 % for
+E5M2), where the relative spacing is coarse, which is what tips the
+element-wise mean towards E5M2.
 """
 import numpy as np
 import pytest
@@ -49,26 +63,38 @@ def table():
     return out
 
 
+EW, NW = 1, 0  # index of the element-wise and the normwise error in a table entry
+
+
 def test_expansion_reduces_error(table):
-    for kind in ("m", "v"):
-        for fmt in (E4, E5):
-            assert table[(kind, fmt, True)][0] < table[(kind, fmt, False)][0]
-    # E4M3 + expansion on the first moment is well below plain E4M3
-    assert table[("m", E4, True)][0] < 0.8 * table[("m", E4, False)][0]
-    assert table[("v", E4, True)][0] < 0.5 * table[("v", E4, False)][0]
+    for metric in (EW, NW):
+        for kind in ("m", "v"):
+            for fmt in (E4, E5):
+                assert table[(kind, fmt, True)][metric] < table[(kind, fmt, False)][metric], (kind, fmt, metric)
+    # E4M3 + expansion well below plain E4M3 (element-wise)
+    assert table[("m", E4, True)][EW] < 0.9 * table[("m", E4, False)][EW]
+    assert table[("v", E4, True)][EW] < 0.5 * table[("v", E4, False)][EW]
 
 
-def test_e4m3_better_for_first_moment(table):
-    assert table[("m", E4, True)][0] < table[("m", E5, True)][0]
-    assert table[("m", E4, False)][0] < table[("m", E5, False)][0]
+def test_first_moment_formats(table):
+    # without expansion E4M3 is the better format for m under both metrics
+    assert table[("m", E4, False)][EW] < table[("m", E5, False)][EW]
+    assert table[("m", E4, False)][NW] < table[("m", E5, False)][NW]
+    # with expansion it holds normwise ...
+    assert table[("m", E4, True)][NW] < table[("m", E5, True)][NW]
+    # ... and is reversed element-wise (a finding, pinned as such)
+    assert table[("m", E5, True)][EW] < table[("m", E4, True)][EW]
 
 
 def test_second_moment_formats(table):
-    # without expansion E4M3 wins clearly ...
-    assert table[("v", E4, False)][0] < 0.75 * table[("v", E5, False)][0]
-    # ... with expansion the two are almost the same (within 10 % of each other)
-    a, b = table[("v", E4, True)][0], table[("v", E5, True)][0]
-    assert abs(a - b) < 0.1 * max(a, b)
+    # without expansion E4M3 wins clearly under both metrics ...
+    for metric in (EW, NW):
+        assert table[("v", E4, False)][metric] < 0.75 * table[("v", E5, False)][metric]
+    # ... with expansion the two are close: within 2 % normwise, 25 % element-wise
+    a, b = table[("v", E4, True)][NW], table[("v", E5, True)][NW]
+    assert abs(a - b) < 0.02 * max(a, b)
+    a, b = table[("v", E4, True)][EW], table[("v", E5, True)][EW]
+    assert abs(a - b) < 0.25 * max(a, b)
 
 
 def test_report(table, capsys):

@@ -213,3 +213,70 @@ def test_fp64_subnormal_members():
     assert np.isfinite(s[0]) and s[0] > 0
     xd = oracle.dequantize(q, s, k, G, E4)
     assert xd[3] == pytest.approx(1e-308, rel=1e-9) and xd[5] == 0.0
+
+
+def test_near_constant_threshold_is_the_rounded_quotient():
+    """k = 1 exactly when the fp64 quotient amax / amin rounds to at most
+    1 + 1e-6 (the constant as fp64): pairs whose rounded quotient is that
+    constant minus two ulps up to plus two ulps, at several scales."""
+    T = 1.0 + 1e-6
+    U = np.spacing(T)
+    rng = np.random.default_rng(5)
+    seen = set()
+    for _ in range(4000):
+        b = float(np.ldexp(1.0 + rng.random(), int(rng.integers(-200, 200))))
+        a = float(b * T)
+        for _k in range(int(rng.integers(0, 5))):
+            a = float(np.nextafter(a, np.inf if rng.random() < 0.5 else -np.inf))
+        off = round((a / b - T) / U)
+        if abs(off) > 2 or a / b != T + off * U:
+            continue
+        seen.add(off)
+        for fmt in (E4, E5):
+            k = oracle.group_k(a, b, fmt)
+            assert (k == 1.0) == (off <= 0), (a, b, off, k)
+    assert seen == {-2, -1, 0, 1, 2}
+
+
+def test_step_poisons_each_moment_on_its_own():
+    """A poisoned stored first moment (s = NaN, codes 0x7F) leaves the second
+    moment's group finite, and the reverse."""
+    G, n = 32, 128
+    rng = np.random.default_rng(6)
+    m = rng.uniform(1e-4, 1e-3, n) * np.where(rng.random(n) < 0.5, -1, 1)
+    v = rng.uniform(1e-8, 1e-7, n)
+    mq, ms, mk = oracle.quantize(m, G, E4)
+    vq, vs, vk = oracle.quantize(v, G, E5)
+    mq[:G], ms[0], mk[0] = 0x7F, np.nan, 1.0
+    vq[2 * G:3 * G], vs[2], vk[2] = 0x7F, np.nan, 1.0
+    p = rng.normal(0, 0.02, n).astype(np.float32)
+    g = (rng.normal(0, 1e-3, n).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    r = oracle.adamw_step(p, g, mq, ms, mk, vq, vs, vk, G, E4, E5, 1e-4, 0.9, 0.95, 1e-8, 0.1, 10)
+    assert np.isnan(r["ms"][0]) and (r["mq"][:G] == 0x7F).all() and np.isfinite(r["vs"][0])
+    assert np.isnan(r["vs"][2]) and (r["vq"][2 * G:3 * G] == 0x7F).all() and np.isfinite(r["ms"][2])
+    assert np.isfinite(r["ms"][[1, 3]]).all() and np.isfinite(r["vs"][[1, 3]]).all()
+    assert np.isnan(r["p"][:G]).all() and np.isfinite(r["p"][G:2 * G]).all()
+
+
+def test_step_with_huge_grads_stays_finite():
+    """Grads near the bf16 maximum give moments beyond the fp32 range but
+    finite in fp64: no group is poisoned and the update equals the dense
+    AdamW of the dequantized state (the quantization being the only other
+    step)."""
+    G, n = 32, 64
+    rng = np.random.default_rng(7)
+    m = rng.uniform(1e-4, 1e-3, n)
+    v = rng.uniform(1e-8, 1e-7, n)
+    mq, ms, mk = oracle.quantize(m, G, E4)
+    vq, vs, vk = oracle.quantize(v, G, E5)
+    gf = rng.normal(0, 1e-3, n).astype(np.float32)
+    gf[:5] = [1e20, -3e20, 3e38, -3.3e38, 2e25]
+    g = (gf.view(np.uint32) >> 16).astype(np.uint16)
+    p = rng.normal(0, 0.02, n).astype(np.float32)
+    r = oracle.adamw_step(p, g, mq, ms, mk, vq, vs, vk, G, E4, E5, 1e-4, 0.9, 0.95, 1e-8, 0.1, 10)
+    assert np.isfinite(r["ms"]).all() and np.isfinite(r["vs"]).all()
+    md = oracle.dequantize(mq, ms, mk, G, E4)
+    vd = oracle.dequantize(vq, vs, vk, G, E5)
+    pd, _, _, _ = oracle.adamw_dense(p, g, md, vd, 1e-4, 0.9, 0.95, 1e-8, 0.1, 10)
+    assert np.array_equal(r["p"], pd)
+    assert np.isfinite(r["p"]).all()
