@@ -24,7 +24,8 @@ FMT_E4M3 = 0
 FMT_E5M2 = 1
 FMT_NO_EXPAND = 0x100
 
-COAT_OK, COAT_EINVAL, COAT_EALIGN, COAT_EHIP = 0, -1, -2, -3
+COAT_OK, COAT_EINVAL, COAT_EALIGN, COAT_EHIP, COAT_ERANGE = 0, -1, -2, -3, -4
+STATIC_MAX_TENSORS = 4096
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcoat_fp8.so")
@@ -69,6 +70,7 @@ def lib() -> ctypes.CDLL:
     L.coat_fp8_adamw_step_planned.argtypes = [ctypes.POINTER(_Plan), i32, i32, i32, *hyper, P]
     L.coat_fp8_adamw_step_multi.argtypes = [ctypes.POINTER(_Tensor), i32, i32, i32, i32, *hyper,
                                             P, ctypes.c_size_t, P]
+    L.coat_fp8_adamw_step_multi_static.argtypes = [ctypes.POINTER(_Tensor), i32, i32, i32, i32, *hyper, P]
     L.coat_fp8_quantize.argtypes = [P, i64, i32, i32, P, P, P, P]
     L.coat_fp8_dequantize.argtypes = [P, P, P, i64, i32, i32, P, P]
     L.coat_fp8_encode.argtypes = [P, i64, i32, P, P]
@@ -79,7 +81,7 @@ def lib() -> ctypes.CDLL:
     L.coat_strerror.restype = ctypes.c_char_p
     L.coat_abi_version.restype = ctypes.c_int
     for name in ("coat_fp8_adamw_step", "coat_multi_plan_init", "coat_fp8_adamw_step_planned",
-                 "coat_fp8_adamw_step_multi", "coat_fp8_quantize", "coat_fp8_dequantize",
+                 "coat_fp8_adamw_step_multi", "coat_fp8_adamw_step_multi_static", "coat_fp8_quantize", "coat_fp8_dequantize",
                  "coat_fp8_encode", "coat_fp8_decode", "coat_fp8_act_quantize",
                  "coat_fp8_act_dequantize"):
         getattr(L, name).restype = ctypes.c_int
@@ -303,6 +305,15 @@ class ParamListState:
         _check(rc, "coat_fp8_adamw_step_multi")
         # keep the workspace alive until the launch has run
         torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+
+    def step_static(self, *, fmt_m: int, fmt_v: int, lr: float, beta1: float, beta2: float,
+                    eps: float, weight_decay: float, step: int, stream=None) -> None:
+        """The same step through the entry point that allocates nothing and
+        keeps its tables in the library's own device array (asynchronous)."""
+        rc = lib().coat_fp8_adamw_step_multi_static(self.descriptors(), len(self.sizes), self.group, fmt_m,
+                                                     fmt_v, lr, beta1, beta2, eps, weight_decay, step,
+                                                     _stream(stream))
+        _check(rc, "coat_fp8_adamw_step_multi_static")
 
     # ------------------------------------------------------------ checkpoint
     #

@@ -28,6 +28,7 @@
 //   * the AdamW update itself (master weights, bf16 copy) runs in fp32;
 //   * the multi-tensor kernel walks a descriptor table of a whole parameter
 //     list in one launch; tiles never span tensors.
+#include <mutex>
 #include <vector>
 
 #include "coat_common.h"
@@ -1785,6 +1786,95 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
+// ------------------------------------------------------------------ static plan tables
+
+// The plan tables of coat_fp8_adamw_step_multi_static: the same layout as a
+// plan workspace (descriptors, full-tile prefix, partial-tile list, each
+// section 256-byte aligned), sized for COAT_STATIC_MAX_TENSORS tensors. Each
+// GPU the library runs on holds its own copy until the process ends. In host
+// code the name is only a stand-in: kernels get the device address that
+// hipGetSymbolAddress returns for the current device.
+namespace {
+constexpr size_t align_up_c(size_t x, size_t a) { return (x + a - 1) / a * a; }
+constexpr size_t kStaticDescBytes = align_up_c(sizeof(TensorRef) * (size_t)COAT_STATIC_MAX_TENSORS, 256);
+constexpr size_t kStaticFbBytes = align_up_c(sizeof(int64_t) * ((size_t)COAT_STATIC_MAX_TENSORS + 1), 256);
+constexpr size_t kStaticPartialBytes = align_up_c(sizeof(int32_t) * (size_t)COAT_STATIC_MAX_TENSORS, 256);
+constexpr size_t kStaticBytes = kStaticDescBytes + kStaticFbBytes + kStaticPartialBytes;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticBytes];
+
+namespace {
+
+// Tables reach the array through kernel arguments (captured at launch, so the
+// host side needs no staging memory and no synchronization), 3 KB per launch.
+constexpr uint32_t kArgChunkBytes = 3072;
+struct alignas(16) ArgChunk {
+    unsigned char data[kArgChunkBytes];
+};
+
+__global__ __launch_bounds__(64) void arg_copy_kernel(ArgChunk chunk, uint32_t bytes, unsigned char* dst) {
+    for (uint32_t i = threadIdx.x * 16u; i < bytes; i += 64u * 16u)
+        *reinterpret_cast<u32x4*>(dst + i) = *reinterpret_cast<const u32x4*>(chunk.data + i);
+}
+
+// Packs consecutive bytes of one table section into argument chunks and
+// enqueues a copy per full chunk; sections are 16-byte aligned and padded.
+class ChunkWriter {
+  public:
+    ChunkWriter(unsigned char* dst, hipStream_t st) : dst_(dst), st_(st) {}
+    void put(const void* src, size_t n) {
+        const unsigned char* p = static_cast<const unsigned char*>(src);
+        while (n > 0) {
+            const size_t take = n < kArgChunkBytes - fill_ ? n : kArgChunkBytes - fill_;
+            memcpy(chunk_.data + fill_, p, take);
+            fill_ += (uint32_t)take;
+            p += take;
+            n -= take;
+            if (fill_ == kArgChunkBytes) flush();
+        }
+    }
+    // the rest of the chunk; the destination's section padding absorbs the round-up to 16 bytes
+    void flush() {
+        if (fill_ == 0) return;
+        const uint32_t bytes = (fill_ + 15u) & ~15u;
+        memset(chunk_.data + fill_, 0, bytes - fill_);
+        hipLaunchKernelGGL(arg_copy_kernel, dim3(1), dim3(64), 0, st_, chunk_, bytes, dst_);
+        if (hipGetLastError() != hipSuccess) ok_ = false;
+        dst_ += bytes;
+        fill_ = 0;
+    }
+    bool ok() const { return ok_; }
+
+  private:
+    ArgChunk chunk_;
+    unsigned char* dst_;
+    hipStream_t st_;
+    uint32_t fill_ = 0;
+    bool ok_ = true;
+};
+
+// The device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int static_tables(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return COAT_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return COAT_EHIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return COAT_OK;
+}
+
+}  // namespace
+
 // ====================================================================== C ABI
 
 extern "C" {
@@ -1797,6 +1887,7 @@ const char* coat_strerror(int status) {
         case COAT_EINVAL: return "invalid argument";
         case COAT_EALIGN: return "pointer not aligned as required (16 bytes for element arrays)";
         case COAT_EHIP: return "HIP runtime error at launch";
+        case COAT_ERANGE: return "more tensors than the library's static plan table holds (COAT_STATIC_MAX_TENSORS)";
         default: return "unknown status";
     }
 }
@@ -1903,6 +1994,60 @@ int coat_fp8_adamw_step_multi(const coat_tensor* tensors, int32_t count, int32_t
     if (rc) return rc;
     return coat_fp8_adamw_step_planned(&plan, group, fmt_m, fmt_v, lr, beta1, beta2, eps, weight_decay, step,
                                        stream);
+}
+
+int coat_fp8_adamw_step_multi_static(const coat_tensor* tensors, int32_t count, int32_t group, int32_t fmt_m,
+                                     int32_t fmt_v, float lr, float beta1, float beta2, float eps,
+                                     float weight_decay, int64_t step, coat_stream_t stream) {
+    if (count < 0 || (count > 0 && !tensors)) return COAT_EINVAL;
+    if (count > COAT_STATIC_MAX_TENSORS) return COAT_ERANGE;
+    StepConsts c;
+    int rc = make_consts(group, fmt_m, fmt_v, lr, beta1, beta2, eps, weight_decay, step, &c);
+    if (rc) return rc;
+    int64_t full = 0, tiles = 0;
+    int32_t n_partial = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        TensorRef t;
+        memcpy(&t, &tensors[i], sizeof(TensorRef));
+        rc = check_tensor(t);
+        if (rc) return rc;
+        full += t.n / kTile;
+        tiles += (t.n + kTile - 1) / kTile;
+        if (t.n % kTile) ++n_partial;
+    }
+    if (tiles == 0) return COAT_OK;
+    void* base = nullptr;
+    rc = static_tables(&base);
+    if (rc) return rc;
+    unsigned char* ws = static_cast<unsigned char*>(base);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    // every byte the step reads is written here first: descriptors [0, count),
+    // prefix [0, count], partial list [0, n_partial); nothing needs clearing
+    ChunkWriter desc(ws, st);
+    desc.put(tensors, sizeof(TensorRef) * (size_t)count);
+    desc.flush();
+    ChunkWriter fbw(ws + kStaticDescBytes, st);
+    int64_t acc = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        fbw.put(&acc, sizeof(acc));
+        acc += tensors[i].n / kTile;
+    }
+    fbw.put(&acc, sizeof(acc));
+    fbw.flush();
+    ChunkWriter pw(ws + kStaticDescBytes + kStaticFbBytes, st);
+    for (int32_t i = 0; i < count; ++i)
+        if (tensors[i].n % kTile) pw.put(&i, sizeof(i));
+    pw.flush();
+    if (!desc.ok() || !fbw.ok() || !pw.ok()) return COAT_EHIP;
+    const TensorRef* dts = reinterpret_cast<const TensorRef*>(ws);
+    const int64_t* dfb = reinterpret_cast<const int64_t*>(ws + kStaticDescBytes);
+    const int32_t* dpt = reinterpret_cast<const int32_t*>(ws + kStaticDescBytes + kStaticFbBytes);
+    const int fm = fmt_m & 0xFF, fv = fmt_v & 0xFF;
+    if (fm == COAT_FMT_E4M3 && fv == COAT_FMT_E4M3) launch_multi<COAT_FMT_E4M3, COAT_FMT_E4M3>(dts, dfb, dpt, count, n_partial, tiles, full, c, st);
+    else if (fm == COAT_FMT_E4M3) launch_multi<COAT_FMT_E4M3, COAT_FMT_E5M2>(dts, dfb, dpt, count, n_partial, tiles, full, c, st);
+    else if (fv == COAT_FMT_E4M3) launch_multi<COAT_FMT_E5M2, COAT_FMT_E4M3>(dts, dfb, dpt, count, n_partial, tiles, full, c, st);
+    else launch_multi<COAT_FMT_E5M2, COAT_FMT_E5M2>(dts, dfb, dpt, count, n_partial, tiles, full, c, st);
+    return launch_status();
 }
 
 int coat_fp8_quantize(const float* x, int64_t n, int32_t group, int32_t fmt, uint8_t* q, double* s,

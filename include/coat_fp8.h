@@ -28,7 +28,8 @@
  *
  * Conventions for every entry point:
  *   - all array pointers are device pointers (HIP device memory) owned by the
- *     caller; the library allocates nothing and keeps no state between calls;
+ *     caller; the library allocates nothing and keeps no state between calls,
+ *     except the device table array of coat_fp8_adamw_step_multi_static;
  *   - work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns without waiting; device-side faults surface at the
  *     caller's next synchronization;
@@ -63,7 +64,8 @@ enum {
     COAT_EINVAL = -1, /* null pointer with n > 0, n < 0, bad group or format, step < 1,
                          non-finite hyperparameter, workspace too small */
     COAT_EALIGN = -2, /* a pointer does not meet the alignment stated above */
-    COAT_EHIP = -3    /* the HIP runtime refused the launch */
+    COAT_EHIP = -3,   /* the HIP runtime refused the launch */
+    COAT_ERANGE = -4  /* more tensors than COAT_STATIC_MAX_TENSORS (static-table entry point) */
 };
 
 /*
@@ -151,6 +153,37 @@ int coat_fp8_adamw_step_multi(const coat_tensor* tensors, int32_t count, int32_t
                               int32_t fmt_m, int32_t fmt_v, float lr, float beta1, float beta2,
                               float eps, float weight_decay, int64_t step, void* workspace,
                               size_t workspace_bytes, coat_stream_t stream);
+
+/* Largest parameter list coat_fp8_adamw_step_multi_static accepts. */
+#define COAT_STATIC_MAX_TENSORS 4096
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * multi-tensor step of coat_fp8_adamw_step_multi with its plan tables kept in
+ * a device array inside the library instead of a caller workspace. It takes
+ * the same arguments minus the workspace, calls no allocator (no hipMalloc,
+ * no hipFree, no host staging buffer) and does not synchronize: it enqueues a
+ * few small copy launches that carry the tables in their kernel arguments,
+ * then the step, all on `stream`, and returns. The result equals
+ * coat_fp8_adamw_step_multi's bit for bit.
+ *   - count <= COAT_STATIC_MAX_TENSORS (4096), else COAT_ERANGE before anything
+ *     is enqueued; other errors as for coat_fp8_adamw_step_multi;
+ *   - each GPU holds one copy of the table array (about 377 KB) from its
+ *     first call until the process ends; it is looked up once per device with
+ *     that device current, so `stream` must belong to the current device;
+ *   - every call on a GPU rewrites that GPU's one array: calls that may
+ *     overlap on one GPU (other streams, other host threads without ordering)
+ *     race, so they must be serialized, e.g. issued on one stream; the array
+ *     keeps the last call's tables, and every entry the step reads is
+ *     written by the call itself, so nothing has to start cleared;
+ *   - the host array `tensors` is read during the call only;
+ *   - COAT_EHIP (a refused launch) may leave the copies before it enqueued.
+ */
+int coat_fp8_adamw_step_multi_static(const coat_tensor* tensors, int32_t count, int32_t group,
+                                     int32_t fmt_m, int32_t fmt_v, float lr, float beta1,
+                                     float beta2, float eps, float weight_decay, int64_t step,
+                                     coat_stream_t stream);
 
 /*
  * Quantize an fp32 array into FP8 state (q, s, k) with per-group dynamic

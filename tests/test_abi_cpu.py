@@ -122,3 +122,25 @@ def test_multi_argument_checks():
     assert L.coat_multi_plan_init(ctypes.byref(plan), arr, 1, FAKE, need, None) == coat.COAT_EALIGN
     assert L.coat_multi_plan_init(ctypes.byref(plan), arr, -1, FAKE, need, None) == coat.COAT_EINVAL
     assert L.coat_fp8_adamw_step_planned(None, 128, 0, 0, *HY, 10, None) == coat.COAT_EINVAL
+
+
+def test_static_multi_argument_checks():
+    L = coat.lib()
+    f = L.coat_fp8_adamw_step_multi_static
+    arr = (coat._Tensor * 2)()
+    arr[0] = coat._Tensor(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1024)
+    arr[1] = coat._Tensor(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0)
+    big = (coat._Tensor * (coat.STATIC_MAX_TENSORS + 1))()
+    assert f(big, coat.STATIC_MAX_TENSORS + 1, 128, 0, 0, *HY, 10, None) == coat.COAT_ERANGE
+    assert "static plan table" in coat.strerror(coat.COAT_ERANGE)
+    assert f(arr, -1, 128, 0, 0, *HY, 10, None) == coat.COAT_EINVAL
+    assert f(None, 1, 128, 0, 0, *HY, 10, None) == coat.COAT_EINVAL
+    assert f(arr, 1, 96, 0, 0, *HY, 10, None) == coat.COAT_EINVAL
+    assert f(arr, 1, 128, 0, 0, *HY, 0, None) == coat.COAT_EINVAL
+    arr[0].m_q = FAKE + 1
+    assert f(arr, 1, 128, 0, 0, *HY, 10, None) == coat.COAT_EALIGN
+    # nothing to do: returns before any device call
+    assert f(arr, 0, 128, 0, 0, *HY, 10, None) == coat.COAT_OK
+    empty = (coat._Tensor * 1)()
+    empty[0] = coat._Tensor(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0)
+    assert f(empty, 1, 128, 0, 0, *HY, 10, None) == coat.COAT_OK
