@@ -7,7 +7,15 @@ resident in HBM (about 133 GB). One step = one multi-tensor launch over the
 whole list. Prints one JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama13b]
-                  [--no-cpu-baseline] [--copy-calibration] [--sweep | --act | --codec]
+                  [--no-cpu-baseline] [--copy-calibration] [--sweep | --act | --codec | --ceiling]
+
+With --ceiling it measures, in one process and on the same resident
+workload, what the step's time is judged against: a plain device copy of
+4 GiB (torch copy_), the memory-only floor of the step's access pattern (the
+instrument in bench_ceiling.hip: the step's bytes in the step's pattern, no
+arithmetic) at the step's residency and at full residency, and the step
+itself, in interleaved rounds; one JSON line per measurement and round, a
+markdown table on stderr.
 
 With --sweep it instead times the step and measures the state codec's
 quantization error for every group size in {32, 64, 128, 256}, format pair
@@ -256,6 +264,158 @@ def codec_bench(args) -> int:
     return 0
 
 
+def resident_state(wl, dev):
+    """Seeded inputs and prior state of a workload, generated on the device."""
+    import torch
+
+    import fp8_optimizer_state_amd as coat
+    import synth
+
+    G = wl.group
+    st = coat.ParamListState(wl.sizes, G, device=dev)
+    for i, n in enumerate(wl.sizes):
+        t = st.tensor(i)
+        synth.params(n, wl.seed, i, device=dev, out=t.params)
+        synth.grads(n, wl.seed, i, device=dev, out=t.grads)
+        m, v = synth.prior_moments(n, G, wl.seed, i, device=dev)
+        coat.quantize(m, t.m_q, t.m_s, t.m_k, group=G, fmt=wl.fmt_m)
+        coat.quantize(v, t.v_q, t.v_s, t.v_k, group=G, fmt=wl.fmt_v)
+        del m, v
+        if i % 60 == 0:
+            log(f"  generated tensor {i}/{len(wl.sizes)}")
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return st
+
+
+def time_copy(dev, reps: int):
+    """Device copy of 2^30 fp32 (4 GiB read + 4 GiB written), HIP events on the
+    copy's stream; returns (ms per copy, GB/s over the bytes moved)."""
+    import torch
+
+    a = torch.empty(1 << 30, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    stream = torch.cuda.current_stream()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return ms, 2.0 * 4.0 * (1 << 30) / (ms * 1e-3) / 1e9
+
+
+def ceiling(args) -> int:
+    """Plain copy, the memory-only floor of the step's pattern and the step,
+    side by side on one resident workload."""
+    import ctypes
+
+    import torch
+
+    import fp8_optimizer_state_amd as coat
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    coat.lib()
+    path = os.path.join(ROOT, "libbench_ceiling.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run python -c 'import __graft_entry__ as g; g.build()'")
+    probe = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    probe.ceiling_pattern_pass.argtypes = [P] * 9 + [ctypes.c_int64, ctypes.c_int, ctypes.c_int, P]
+    probe.ceiling_pattern_pass.restype = ctypes.c_int
+    probe.ceiling_copy_pass.argtypes = [P, P, ctypes.c_int64, P]
+    probe.ceiling_read_pass.argtypes = [P, ctypes.c_int64, P, P]
+    probe.ceiling_write_pass.argtypes = [P, ctypes.c_int64, P]
+    for f in (probe.ceiling_copy_pass, probe.ceiling_read_pass, probe.ceiling_write_pass):
+        f.restype = ctypes.c_int
+    G = wl.group
+    lg = G.bit_length() - 1
+    log(f"ceiling: workload {wl.name}")
+    st = resident_state(wl, dev)
+    # the probe walks the flat buffers as one tensor of whole tiles; every group
+    # it touches is a group of the list
+    n_probe = st.n_padded // 1024 * 1024
+    assert n_probe // G <= st.n_groups and n_probe <= st.n_padded
+    h = synth.HYPER
+    hy = dict(fmt_m=wl.fmt_m, fmt_v=wl.fmt_v, lr=h["lr"], beta1=h["b1"], beta2=h["b2"], eps=h["eps"],
+              weight_decay=h["wd"])
+    st.plan()
+    stream = torch.cuda.current_stream()
+    step_lds = 37688  # the table kernel's LDS per block: four blocks per CU
+    bpp = wl.bytes_per_param()
+    step_no = [h["step"]]
+
+    def probe_pass(lds):
+        rc = probe.ceiling_pattern_pass(st.params.data_ptr(), st.params_bf16.data_ptr(), st.grads.data_ptr(),
+                                        st.m_q.data_ptr(), st.v_q.data_ptr(), st.m_s.data_ptr(), st.m_k.data_ptr(),
+                                        st.v_s.data_ptr(), st.v_k.data_ptr(), n_probe, lg, lds, stream.cuda_stream)
+        assert rc == 0, rc
+
+    def step_once():
+        st.step(step=step_no[0], **hy)
+        step_no[0] += 1
+
+    # plain streams over 4 GiB buffers (copy: 4 GiB read + 4 GiB written)
+    bufa = torch.ones(1 << 30, dtype=torch.float32, device=dev)
+    bufb = torch.empty_like(bufa)
+    word = torch.zeros(4, dtype=torch.int32, device=dev)
+    n16 = bufa.numel() // 4
+    gib4 = 4.0 * (1 << 30)
+
+    def plain(rc):
+        assert rc == 0, rc
+
+    kinds = (("read 4 GiB", lambda: plain(probe.ceiling_read_pass(bufa.data_ptr(), n16, word.data_ptr(),
+                                                                  stream.cuda_stream)), gib4),
+             ("write 4 GiB", lambda: plain(probe.ceiling_write_pass(bufb.data_ptr(), n16, stream.cuda_stream)), gib4),
+             ("copy 4 GiB (probe kernel)", lambda: plain(probe.ceiling_copy_pass(bufa.data_ptr(), bufb.data_ptr(), n16,
+                                                                               stream.cuda_stream)), 2 * gib4),
+             ("pattern floor, step residency", lambda: probe_pass(step_lds), bpp * n_probe),
+             ("pattern floor, full residency", lambda: probe_pass(0), bpp * n_probe),
+             ("step", step_once, bpp * wl.n_params))
+    for _, fn, _ in kinds:
+        for _ in range(args.warmup):
+            fn()
+    torch.cuda.synchronize()
+    rows = {"copy 4 GiB (torch copy_)": []}
+    rows.update({name: [] for name, _, _ in kinds})
+    rounds = 3
+    for r in range(rounds):
+        ms, gbps = time_copy(dev, args.steps)
+        rows["copy 4 GiB (torch copy_)"].append((ms, gbps))
+        print(json.dumps({"ceiling": "copy 4 GiB (torch copy_)", "round": r, "ms": ms, "GBps": gbps,
+                          "frac_of_8TBps": gbps / PEAK_HBM_GBPS}), flush=True)
+        for name, fn, nbytes in kinds:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            rows[name].append((ms, gbps))
+            print(json.dumps({"ceiling": name, "round": r, "workload": wl.name, "ms": ms, "GBps": gbps,
+                              "frac_of_8TBps": gbps / PEAK_HBM_GBPS}), flush=True)
+        log(f"round {r} done")
+    log(f"| measurement ({wl.name}) | ms (mean of {rounds} rounds x {args.steps}) | GB/s | % of 8 TB/s |")
+    log("|---|---|---|---|")
+    for name, vals in rows.items():
+        ms = sum(v[0] for v in vals) / len(vals)
+        gb = sum(v[1] for v in vals) / len(vals)
+        log(f"| {name} | {ms:.3f} | {gb:.0f} | {100 * gb / PEAK_HBM_GBPS:.1f} |")
+    return 0
+
+
 def cpu_baseline(wl, per_tensor: int = 229376) -> dict:
     """The oracle, single-threaded, on a bounded sample of the workload: the
     first `per_tensor` elements of every tensor (about 65M params for the
@@ -316,6 +476,8 @@ def main() -> int:
     ap.add_argument("--act", action="store_true", help="time the FP8 activation codec instead of the step")
     ap.add_argument("--codec", action="store_true",
                     help="time the FP8 state codec (quantize / dequantize of moments) instead of the step")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="time a plain copy, the memory-only floor of the step's pattern and the step side by side")
     args = ap.parse_args()
     if args.steps < 1 or args.warmup < 0:
         print("bench.py needs --steps >= 1 and --warmup >= 0", file=sys.stderr)
@@ -331,6 +493,8 @@ def main() -> int:
         return act_bench(args)
     if args.codec:
         return codec_bench(args)
+    if args.ceiling:
+        return ceiling(args)
 
     import torch
 
@@ -346,19 +510,7 @@ def main() -> int:
 
     # ---- resident state and inputs, generated on the device
     t0 = time.perf_counter()
-    st = coat.ParamListState(wl.sizes, G, device=dev)
-    for i, n in enumerate(wl.sizes):
-        t = st.tensor(i)
-        synth.params(n, wl.seed, i, device=dev, out=t.params)
-        synth.grads(n, wl.seed, i, device=dev, out=t.grads)
-        m, v = synth.prior_moments(n, G, wl.seed, i, device=dev)
-        coat.quantize(m, t.m_q, t.m_s, t.m_k, group=G, fmt=wl.fmt_m)
-        coat.quantize(v, t.v_q, t.v_s, t.v_k, group=G, fmt=wl.fmt_v)
-        del m, v
-        if i % 60 == 0:
-            log(f"  generated tensor {i}/{len(wl.sizes)}")
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
+    st = resident_state(wl, dev)
     log(f"inputs resident in {time.perf_counter() - t0:.1f} s; "
         f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
 
@@ -388,15 +540,13 @@ def main() -> int:
     ms_median, ms_min = per_step[len(per_step) // 2], per_step[0]
     log(f"timed {args.steps} steps: {ms:.3f} ms/step (median {ms_median:.3f}, min {ms_min:.3f})")
 
+    copy = None
     if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.float32, device=dev)  # 4 GiB read, 4 GiB written
-        b = torch.empty_like(a)
-        a.fill_(1.0)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
-        log("copy calibration: 4 GiB fp32 copy done")
+        # a device copy of known size, for the counter calibration, timed as well
+        copy_ms, copy_gbps = time_copy(dev, 5)
+        copy = {"bytes": 2 * 4 * (1 << 30), "ms": copy_ms, "GBps": copy_gbps,
+                "frac_of_8TBps": copy_gbps / PEAK_HBM_GBPS}
+        log(f"copy calibration: 4 GiB fp32 copy, {copy_ms:.3f} ms, {copy_gbps:.0f} GB/s")
 
     n = wl.n_params
     bpp = wl.bytes_per_param()
@@ -442,9 +592,15 @@ def main() -> int:
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS,
             "traffic": traffic,
+            "traffic_source": (f"rocprofv3 FETCH_SIZE and WRITE_SIZE runs committed in "
+                               f"{os.path.relpath(PMC_FILE, ROOT)}, taken on kernel source sha256 "
+                               f"{kernel_source_hash()[:16]}; not measured in this run")
+            if traffic is not None else "null: no committed counter run matches this kernel source and workload",
         },
         "cpu_baseline": cpu,
     }
+    if copy is not None:
+        out["copy_calibration"] = copy
     print(json.dumps(out), flush=True)
     return 0
 

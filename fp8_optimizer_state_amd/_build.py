@@ -36,5 +36,19 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_ceiling_probe() -> str:
+    """Compile bench_ceiling.hip (the memory-pattern instrument of bench.py
+    --ceiling, not part of the library) into libbench_ceiling.so at the root."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    out = os.path.join(ROOT, "libbench_ceiling.so")
+    flags = [f for f in HIPCC_FLAGS if f != "-ffp-contract=off"]
+    res = subprocess.run([hipcc, *flags, "-o", out + ".tmp", os.path.join(ROOT, "bench_ceiling.hip")],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
