@@ -151,9 +151,17 @@ __device__ __forceinline__ double rcp_f64(double b) {
     return r;
 }
 
-// a/b for finite normal b, within an ulp.
+// 1/b to about 2^-48 (one Newton step on the hardware estimate, which is good
+// to about 2^-24): enough before a correction step or a rounding to fp32.
+__device__ __forceinline__ double rcp_f64_1(double b) {
+    const double r = __builtin_amdgcn_rcp(b);
+    return __builtin_fma(__builtin_fma(-b, r, 1.0), r, r);
+}
+
+// a/b for finite normal b, within an ulp (the final correction step takes the
+// quotient from the reciprocal's 2^-48 to full precision).
 __device__ __forceinline__ double div_f64(double a, double b) {
-    const double r = rcp_f64(b);
+    const double r = rcp_f64_1(b);
     const double q = a * r;
     return __builtin_fma(__builtin_fma(-b, q, a), r, q);
 }
@@ -526,11 +534,11 @@ constexpr uint32_t kSlow = 2u;    // fp32 fast path unsafe for this group: exact
 // k = ln R_fp8 / ln(amax / amin) (= log2 R_fp8 / log2 R), k = 1 for an
 // all-zero or near-constant group or without expansion; then the range guard:
 // amax^k and amax^k / R_fp8 within [2^-1022, 2^1023]; s = amax^k / fpmax.
-// log2 of x (hi + lo) for finite x > 0; 0 for anything else (values a caller
-// does not use: zero or infinite statistics of empty or poisoned groups).
+// log2 of x (hi + lo) for finite x > 0. For 0 or a non-finite x (the
+// statistics of all-zero and poisoned groups) the result is meaningless and
+// unused: new_group overrides everything it feeds for those groups.
 __device__ __forceinline__ double log2_stat(double x, double& lo) {
-    const double xs = (x > 0.0 && x < __builtin_inf()) ? x : 1.0;
-    return log2_full_dd(xs, lo);
+    return log2_full_dd(x, lo);
 }
 
 // Whether the correctly rounded fp64 quotient a / b exceeds T = 1 + 1e-6 (the
@@ -560,29 +568,18 @@ __device__ NewGroup new_group(double amax, double amin, double L, double L_lo, d
                               bool poison, bool expand, const FmtRT& F) {
     NewGroup g;
     g.amax = amax;
-    g.flags = 0;
-    g.r = 1.0;
-    g.w = 0.0f;
-    if (poison) {
-        g.s = __builtin_nan("");
-        g.k = 1.0f;
-        g.ia = 0.0f;
-        g.flags = kPoison;
-        return g;
-    }
-    if (amax == 0.0) {
-        g.s = 0.0;
-        g.k = 1.0f;
-        g.ia = 0.0f;
-        return g;
-    }
+    // Poisoned and all-zero groups are rare: the common path below runs for
+    // every lane (its values for those groups are meaningless: L and Lm are
+    // then unusable and 1/amax infinite), the range guard is kept from them,
+    // and their fields are overridden in a wave-uniform branch at the end.
+    const bool rare = poison || amax == 0.0;
     float k = 1.0f;
     const double d = L - Lm;
     const double log2R = d + (((L - d) - Lm) + (L_lo - Lm_lo));
-    if (expand && ratio_above_near_constant(amax, amin)) k = (float)(F.log2_rf * rcp_f64(log2R));
+    if (expand && !rare && ratio_above_near_constant(amax, amin)) k = (float)(F.log2_rf * rcp_f64(log2R));
     const double lo = -1022.0 + F.log2_rf, hi = 1023.0;
     const double kL = (double)k * L;
-    if (!(kL >= lo && kL <= hi)) {
+    if (!rare && !(kL >= lo && kL <= hi)) {
         asm volatile("");  // rare: not to be computed speculatively on the common path
         const double bound = (L < 0.0) ? lo / L : hi / L;
         float kk = (float)bound;
@@ -595,11 +592,21 @@ __device__ NewGroup new_group(double amax, double amin, double L, double L_lo, d
     g.k = k;
     g.r = rcp_f64((double)k);
     g.s = exp2_full((double)k * L - F.log2_fpmax);
-    g.ia = (float)rcp_f64(amax);
+    g.ia = (float)rcp_f64_1(amax);
     g.w = __builtin_fmaf(kAmbW1, k, F.amb_w0);
     // The fp32 path needs every member and 1/amax normal in fp32 and |x| / amax
     // at least 2^-100 for nonzero members.
-    if (!(amax <= 0x1p126 && amin >= 0x1p-126 && log2R <= 100.0)) g.flags = kSlow;
+    g.flags = (amax <= 0x1p126 && amin >= 0x1p-126 && log2R <= 100.0) ? 0u : kSlow;
+    if (__builtin_expect(__any(rare), 0)) {
+        if (rare) {
+            g.s = poison ? __builtin_nan("") : 0.0;
+            g.k = 1.0f;
+            g.r = 1.0;
+            g.ia = 0.0f;
+            g.w = 0.0f;
+            g.flags = poison ? kPoison : 0u;
+        }
+    }
     return g;
 }
 
@@ -1331,8 +1338,16 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
         cm[i] = fast_codes4<FM>(xm + 4 * i, nm, am[i]);
         cv[i] = fast_codes4<FV>(xv + 4 * i, nv, av[i]);
     }
-    if (nm.flags & kSlow) { am[0] = am[1] = am[2] = am[3] = 0x80808080u; }
-    if (nv.flags & kSlow) { av[0] = av[1] = av[2] = av[3] = 0x80808080u; }
+    // Groups outside the fp32 path's range (every element decided exactly) or
+    // poisoned (no element decided; every code NaN) are rare: their flags are
+    // applied in a wave-uniform branch, so that a tile without them spends no
+    // selects on them.
+    const bool flagged = (nm.flags | nv.flags) != 0u;
+    const bool any_flagged = __builtin_expect(__any(flagged), 0);
+    if (any_flagged) {
+        if (nm.flags & kSlow) { am[0] = am[1] = am[2] = am[3] = 0x80808080u; }
+        if (nv.flags & kSlow) { av[0] = av[1] = av[2] = av[3] = 0x80808080u; }
+    }
     if (nvalid < kLaneElems) {  // never redo elements past the end
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1343,8 +1358,10 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
             av[i] &= keep;
         }
     }
-    if (nm.flags & kPoison) { am[0] = am[1] = am[2] = am[3] = 0u; }
-    if (nv.flags & kPoison) { av[0] = av[1] = av[2] = av[3] = 0u; }
+    if (any_flagged) {
+        if (nm.flags & kPoison) { am[0] = am[1] = am[2] = am[3] = 0u; }
+        if (nv.flags & kPoison) { av[0] = av[1] = av[2] = av[3] = 0u; }
+    }
     if (__any((am[0] | am[1] | am[2] | am[3] | av[0] | av[1] | av[2] | av[3]) != 0u)) {
         if (pair) {  // the other moment's exact-path fields, from the partner lane
             const double oa = dpp64<kDppXor1>(own_amax), orr = dpp64<kDppXor1>(own_r);
@@ -1358,8 +1375,10 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
         redo_ambiguous<FM>(am, cm, pk.mq, pk, pm, nm, lq_m, ct.lqm[0], fm, c.c1, false, cf);
         redo_ambiguous<FV>(av, cv, pk.vq, pk, pv, nv, lq_v, ct.lqm[1], fv, c.c2, true, cf);
     }
-    if (nm.flags & kPoison) { cm[0] = cm[1] = cm[2] = cm[3] = 0x7F7F7F7Fu; }
-    if (nv.flags & kPoison) { cv[0] = cv[1] = cv[2] = cv[3] = 0x7F7F7F7Fu; }
+    if (any_flagged) {
+        if (nm.flags & kPoison) { cm[0] = cm[1] = cm[2] = cm[3] = 0x7F7F7F7Fu; }
+        if (nv.flags & kPoison) { cv[0] = cv[1] = cv[2] = cv[3] = 0x7F7F7F7Fu; }
+    }
 
     // ---- store codes
     if (nvalid == kLaneElems) {
