@@ -1,7 +1,8 @@
 // Definitions shared by the HIP sources of the library: vector and address
 // space types, the tiling constants, the FP8 formats (OCP E4M3FN and E5M2; bit
 // layouts per the FP8 guide on maplevalley.com.cn, section "format choice"),
-// cross-lane moves, the exact FP8 encode and decode, and host-side helpers.
+// cross-lane moves, the exact FP8 encode and decode, and the launch helpers
+// (argument checks and plan tables are in coat_host.h).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,6 +12,7 @@
 #include <string.h>
 
 #include "coat_fp8.h"
+#include "coat_host.h"
 
 namespace {
 
@@ -199,21 +201,6 @@ __device__ __forceinline__ int64_t wave_id() {
 }
 
 // ------------------------------------------------------------------ host side
-
-inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-inline int lg2_group_of(int32_t group) {
-    if (group < 16 || group > 1024 || (group & (group - 1)) != 0) return -1;
-    int l = 0;
-    while ((1 << l) < group) ++l;
-    return l;
-}
-
-inline bool fmt_ok(int32_t fmt) {
-    const int base = fmt & 0xFF;
-    return (base == COAT_FMT_E4M3 || base == COAT_FMT_E5M2) && (fmt & ~(0xFF | COAT_FMT_NO_EXPAND)) == 0;
-}
 
 inline int device_cus() {
     int dev = 0, cus = 0;

@@ -695,29 +695,7 @@ __device__ __forceinline__ uint32_t fast_codes4(const float* xf, const NewGroup&
 
 // ------------------------------------------------------------------ step
 
-struct StepConsts {
-    double b1, c1, b2, c2;  // moment coefficients (c = 1 - b), fp64
-    float decay;            // 1 - lr wd
-    float ssz;              // lr / (1 - b1^t)
-    float ib2;              // 1 / sqrt(1 - b2^t)
-    float eps;
-    int lg2_group;
-    int expand_m, expand_v;
-};
-
-struct TensorRef {
-    float* p;
-    uint16_t* w;
-    const uint16_t* g;
-    uint8_t* mq;
-    double* ms;
-    float* mk;
-    uint8_t* vq;
-    double* vs;
-    float* vk;
-    int64_t n;
-};
-static_assert(sizeof(TensorRef) == sizeof(coat_tensor), "descriptor layout");
+static_assert(kTile == kPlanTile, "tile size of the plan tables");
 
 // Dequantize byte i of code word w: returns the magnitude
 // 2^(LQ[c] r + a + a_lo) and sets tb to the code's table factor (+/- b), so
@@ -1714,43 +1692,6 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const uint8_t* __restric
 // block's table set-up starts to cost more than the finer balance gains.
 constexpr int kStepBlocksPerCU = 256;
 
-bool finite_f(float x) { return x == x && x - x == 0.0f; }
-
-int make_consts(int32_t group, int32_t fmt_m, int32_t fmt_v, float lr, float b1, float b2, float eps,
-                float wd, int64_t step, StepConsts* c) {
-    const int lg = lg2_group_of(group);
-    if (lg < 0 || !fmt_ok(fmt_m) || !fmt_ok(fmt_v) || step < 1) return COAT_EINVAL;
-    if (!finite_f(lr) || !finite_f(b1) || !finite_f(b2) || !finite_f(eps) || !finite_f(wd)) return COAT_EINVAL;
-    const double t = (double)step;
-    const double bc1 = 1.0 - pow((double)b1, t);
-    const double bc2 = 1.0 - pow((double)b2, t);
-    if (!(bc1 != 0.0) || !(bc2 > 0.0)) return COAT_EINVAL;
-    c->b1 = (double)b1;
-    c->c1 = 1.0 - (double)b1;
-    c->b2 = (double)b2;
-    c->c2 = 1.0 - (double)b2;
-    c->decay = (float)(1.0 - (double)lr * (double)wd);
-    c->ssz = (float)((double)lr / bc1);
-    c->ib2 = (float)(1.0 / sqrt(bc2));
-    c->eps = eps;
-    c->lg2_group = lg;
-    c->expand_m = (fmt_m & COAT_FMT_NO_EXPAND) ? 0 : 1;
-    c->expand_v = (fmt_v & COAT_FMT_NO_EXPAND) ? 0 : 1;
-    return COAT_OK;
-}
-
-int check_tensor(const TensorRef& t) {
-    if (t.n < 0) return COAT_EINVAL;
-    if (t.n == 0) return COAT_OK;
-    if (!t.p || !t.g || !t.mq || !t.ms || !t.mk || !t.vq || !t.vs || !t.vk) return COAT_EINVAL;
-    if (!aligned16(t.p) || !aligned16(t.g) || !aligned16(t.mq) || !aligned16(t.vq) ||
-        (t.w && !aligned16(t.w)) || !aligned(t.ms, 8) || !aligned(t.vs, 8) || !aligned(t.mk, 4) ||
-        !aligned(t.vk, 4))
-        return COAT_EALIGN;
-    return COAT_OK;
-}
-
-
 // Groups of 128 and more: the whole tiles run in the table kernel, then a
 // direct-path launch covers any partial tiles. Otherwise one direct-path launch.
 template <int FM, int FV>
@@ -1801,8 +1742,6 @@ void launch_multi(const TensorRef* ts, const int64_t* fb, const int32_t* partial
         launch_multi_lg<FM, FV, false, 0>(ts, fb, partial, count, n_partial, n_partial, c, kPhasePartial, st);
 }
 
-size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
 }  // namespace
 
 // ------------------------------------------------------------------ static plan tables
@@ -1813,64 +1752,25 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // GPU the library runs on holds its own copy until the process ends. In host
 // code the name is only a stand-in: kernels get the device address that
 // hipGetSymbolAddress returns for the current device.
-namespace {
-constexpr size_t align_up_c(size_t x, size_t a) { return (x + a - 1) / a * a; }
-constexpr size_t kStaticDescBytes = align_up_c(sizeof(TensorRef) * (size_t)COAT_STATIC_MAX_TENSORS, 256);
-constexpr size_t kStaticFbBytes = align_up_c(sizeof(int64_t) * ((size_t)COAT_STATIC_MAX_TENSORS + 1), 256);
-constexpr size_t kStaticPartialBytes = align_up_c(sizeof(int32_t) * (size_t)COAT_STATIC_MAX_TENSORS, 256);
-constexpr size_t kStaticBytes = kStaticDescBytes + kStaticFbBytes + kStaticPartialBytes;
-}  // namespace
-
-static __device__ __align__(256) unsigned char scratch[kStaticBytes];
+static __device__ __align__(256) unsigned char scratch[kStaticLayout.total];
 
 namespace {
 
-// Tables reach the array through kernel arguments (captured at launch, so the
-// host side needs no staging memory and no synchronization), 3 KB per launch.
-constexpr uint32_t kArgChunkBytes = 3072;
-struct alignas(16) ArgChunk {
-    unsigned char data[kArgChunkBytes];
-};
-
+// The tables reach the array through kernel arguments (captured at launch, so
+// the host side needs no staging memory and no synchronization).
 __global__ __launch_bounds__(64) void arg_copy_kernel(ArgChunk chunk, uint32_t bytes, unsigned char* dst) {
     for (uint32_t i = threadIdx.x * 16u; i < bytes; i += 64u * 16u)
         *reinterpret_cast<u32x4*>(dst + i) = *reinterpret_cast<const u32x4*>(chunk.data + i);
 }
 
-// Packs consecutive bytes of one table section into argument chunks and
-// enqueues a copy per full chunk; sections are 16-byte aligned and padded.
-class ChunkWriter {
-  public:
-    ChunkWriter(unsigned char* dst, hipStream_t st) : dst_(dst), st_(st) {}
-    void put(const void* src, size_t n) {
-        const unsigned char* p = static_cast<const unsigned char*>(src);
-        while (n > 0) {
-            const size_t take = n < kArgChunkBytes - fill_ ? n : kArgChunkBytes - fill_;
-            memcpy(chunk_.data + fill_, p, take);
-            fill_ += (uint32_t)take;
-            p += take;
-            n -= take;
-            if (fill_ == kArgChunkBytes) flush();
-        }
+// ChunkWriter's sink for the device array: one copy launch per chunk.
+struct LaunchSink {
+    unsigned char* base;
+    hipStream_t st;
+    bool operator()(const ArgChunk& chunk, uint32_t bytes, size_t offset) {
+        hipLaunchKernelGGL(arg_copy_kernel, dim3(1), dim3(64), 0, st, chunk, bytes, base + offset);
+        return hipGetLastError() == hipSuccess;
     }
-    // the rest of the chunk; the destination's section padding absorbs the round-up to 16 bytes
-    void flush() {
-        if (fill_ == 0) return;
-        const uint32_t bytes = (fill_ + 15u) & ~15u;
-        memset(chunk_.data + fill_, 0, bytes - fill_);
-        hipLaunchKernelGGL(arg_copy_kernel, dim3(1), dim3(64), 0, st_, chunk_, bytes, dst_);
-        if (hipGetLastError() != hipSuccess) ok_ = false;
-        dst_ += bytes;
-        fill_ = 0;
-    }
-    bool ok() const { return ok_; }
-
-  private:
-    ArgChunk chunk_;
-    unsigned char* dst_;
-    hipStream_t st_;
-    uint32_t fill_ = 0;
-    bool ok_ = true;
 };
 
 // The device address of `scratch` on the current device, looked up once per
@@ -1931,13 +1831,11 @@ int coat_fp8_adamw_step(float* params, uint16_t* params_bf16, const uint16_t* gr
     return launch_status();
 }
 
-// Workspace layout: descriptors, the full-tile prefix (count + 1 int64), the
-// indices of tensors with a partial last tile (count int32), each section
-// 256-byte aligned.
+// Workspace layout: plan_layout (descriptors, the full-tile prefix, the
+// indices of tensors with a partial last tile, each section 256-byte aligned).
 size_t coat_multi_workspace_bytes(int32_t count) {
     if (count < 0) return 0;
-    return align_up(sizeof(TensorRef) * (size_t)count, 256) + align_up(sizeof(int64_t) * ((size_t)count + 1), 256) +
-           align_up(sizeof(int32_t) * (size_t)count, 256);
+    return plan_layout((size_t)count).total;
 }
 
 int coat_multi_plan_init(coat_multi_plan* plan, const coat_tensor* tensors, int32_t count, void* workspace,
@@ -1945,34 +1843,19 @@ int coat_multi_plan_init(coat_multi_plan* plan, const coat_tensor* tensors, int3
     if (!plan || count < 0 || (count > 0 && !tensors)) return COAT_EINVAL;
     if (!workspace || workspace_bytes < coat_multi_workspace_bytes(count)) return COAT_EINVAL;
     if (!aligned(workspace, 256)) return COAT_EALIGN;
-    const size_t desc_bytes = align_up(sizeof(TensorRef) * (size_t)count, 256);
-    const size_t fb_bytes = align_up(sizeof(int64_t) * ((size_t)count + 1), 256);
     const size_t total = coat_multi_workspace_bytes(count);
-    std::vector<char> host(total, 0);
-    TensorRef* hd = reinterpret_cast<TensorRef*>(host.data());
-    int64_t* fb = reinterpret_cast<int64_t*>(host.data() + desc_bytes);
-    int32_t* partial = reinterpret_cast<int32_t*>(host.data() + desc_bytes + fb_bytes);
-    int64_t full = 0, tiles = 0, n_total = 0;
-    int32_t n_partial = 0;
-    for (int32_t i = 0; i < count; ++i) {
-        memcpy(&hd[i], &tensors[i], sizeof(TensorRef));
-        const int rc = check_tensor(hd[i]);
-        if (rc) return rc;
-        fb[i] = full;
-        full += hd[i].n / kTile;
-        if (hd[i].n % kTile) partial[n_partial++] = i;
-        tiles += (hd[i].n + kTile - 1) / kTile;
-        n_total += hd[i].n;
-    }
-    fb[count] = full;
+    std::vector<unsigned char> host(total);
+    PlanSummary sum;
+    const int rc = fill_plan(tensors, count, host.data(), host.size(), &sum);
+    if (rc) return rc;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (hipMemcpyAsync(workspace, host.data(), total, hipMemcpyHostToDevice, st) != hipSuccess) return COAT_EHIP;
     if (hipStreamSynchronize(st) != hipSuccess) return COAT_EHIP;
     plan->workspace = workspace;
     plan->count = count;
-    plan->tiles = tiles;
-    plan->n_total = n_total;
-    plan->n_partial = n_partial;
+    plan->tiles = sum.tiles;
+    plan->n_total = sum.n_total;
+    plan->n_partial = sum.n_partial;
     return COAT_OK;
 }
 
@@ -1985,12 +1868,11 @@ int coat_fp8_adamw_step_planned(const coat_multi_plan* plan, int32_t group, int3
     if (rc) return rc;
     if (plan->count == 0 || plan->tiles == 0) return COAT_OK;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const size_t desc_bytes = align_up(sizeof(TensorRef) * (size_t)plan->count, 256);
-    const size_t fb_bytes = align_up(sizeof(int64_t) * ((size_t)plan->count + 1), 256);
+    const PlanLayout L = plan_layout((size_t)plan->count);
     const char* ws = static_cast<const char*>(plan->workspace);
-    const TensorRef* dts = reinterpret_cast<const TensorRef*>(ws);
-    const int64_t* dfb = reinterpret_cast<const int64_t*>(ws + desc_bytes);
-    const int32_t* dpt = reinterpret_cast<const int32_t*>(ws + desc_bytes + fb_bytes);
+    const TensorRef* dts = reinterpret_cast<const TensorRef*>(ws + L.desc);
+    const int64_t* dfb = reinterpret_cast<const int64_t*>(ws + L.fb);
+    const int32_t* dpt = reinterpret_cast<const int32_t*>(ws + L.partial);
     const int fm = fmt_m & 0xFF, fv = fmt_v & 0xFF;
     const int count = plan->count, np = plan->n_partial;
     const int64_t tiles = plan->tiles, full = plan->tiles - plan->n_partial;
@@ -2023,44 +1905,23 @@ int coat_fp8_adamw_step_multi_static(const coat_tensor* tensors, int32_t count, 
     StepConsts c;
     int rc = make_consts(group, fmt_m, fmt_v, lr, beta1, beta2, eps, weight_decay, step, &c);
     if (rc) return rc;
-    int64_t full = 0, tiles = 0;
-    int32_t n_partial = 0;
-    for (int32_t i = 0; i < count; ++i) {
-        TensorRef t;
-        memcpy(&t, &tensors[i], sizeof(TensorRef));
-        rc = check_tensor(t);
-        if (rc) return rc;
-        full += t.n / kTile;
-        tiles += (t.n + kTile - 1) / kTile;
-        if (t.n % kTile) ++n_partial;
-    }
-    if (tiles == 0) return COAT_OK;
+    PlanSummary sum;
+    rc = scan_tensors(tensors, count, &sum);
+    if (rc) return rc;
+    if (sum.tiles == 0) return COAT_OK;
     void* base = nullptr;
     rc = static_tables(&base);
     if (rc) return rc;
     unsigned char* ws = static_cast<unsigned char*>(base);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    // every byte the step reads is written here first: descriptors [0, count),
-    // prefix [0, count], partial list [0, n_partial); nothing needs clearing
-    ChunkWriter desc(ws, st);
-    desc.put(tensors, sizeof(TensorRef) * (size_t)count);
-    desc.flush();
-    ChunkWriter fbw(ws + kStaticDescBytes, st);
-    int64_t acc = 0;
-    for (int32_t i = 0; i < count; ++i) {
-        fbw.put(&acc, sizeof(acc));
-        acc += tensors[i].n / kTile;
-    }
-    fbw.put(&acc, sizeof(acc));
-    fbw.flush();
-    ChunkWriter pw(ws + kStaticDescBytes + kStaticFbBytes, st);
-    for (int32_t i = 0; i < count; ++i)
-        if (tensors[i].n % kTile) pw.put(&i, sizeof(i));
-    pw.flush();
-    if (!desc.ok() || !fbw.ok() || !pw.ok()) return COAT_EHIP;
-    const TensorRef* dts = reinterpret_cast<const TensorRef*>(ws);
-    const int64_t* dfb = reinterpret_cast<const int64_t*>(ws + kStaticDescBytes);
-    const int32_t* dpt = reinterpret_cast<const int32_t*>(ws + kStaticDescBytes + kStaticFbBytes);
+    // every byte the step reads is written here first; nothing needs clearing
+    LaunchSink sink{ws, st};
+    if (!write_static_tables(tensors, count, sink)) return COAT_EHIP;
+    const TensorRef* dts = reinterpret_cast<const TensorRef*>(ws + kStaticLayout.desc);
+    const int64_t* dfb = reinterpret_cast<const int64_t*>(ws + kStaticLayout.fb);
+    const int32_t* dpt = reinterpret_cast<const int32_t*>(ws + kStaticLayout.partial);
+    const int n_partial = sum.n_partial;
+    const int64_t tiles = sum.tiles, full = sum.full;
     const int fm = fmt_m & 0xFF, fv = fmt_v & 0xFF;
     if (fm == COAT_FMT_E4M3 && fv == COAT_FMT_E4M3) launch_multi<COAT_FMT_E4M3, COAT_FMT_E4M3>(dts, dfb, dpt, count, n_partial, tiles, full, c, st);
     else if (fm == COAT_FMT_E4M3) launch_multi<COAT_FMT_E4M3, COAT_FMT_E5M2>(dts, dfb, dpt, count, n_partial, tiles, full, c, st);
