@@ -44,9 +44,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
-PMC_FILE = os.path.join(ROOT, "profiles", "coat_step_multi_llama13b_pmc.json")
+
+
+def pmc_file(workload: str) -> str:
+    """The committed rocprofv3 counter summary (HBM bytes) of a workload's step kernel."""
+    return os.path.join(ROOT, "profiles", f"coat_step_multi_{workload}_pmc.json")
+
+
 # the sources the step kernel is built from (the activation codec is not one)
-KERNEL_SRCS = [os.path.join(ROOT, "fp8_optimizer_state_amd", "csrc", f) for f in ("coat_common.h", "coat_fp8.hip")]
+KERNEL_SRCS = [os.path.join(ROOT, "fp8_optimizer_state_amd", "csrc", f)
+               for f in ("coat_common.h", "coat_host.h", "coat_fp8.hip")]
 
 
 def log(msg: str) -> None:
@@ -66,7 +73,7 @@ def load_traffic(workload: str, n_launch_bytes: float):
     """HBM traffic per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
     try:
-        with open(PMC_FILE) as f:
+        with open(pmc_file(workload)) as f:
             pmc = json.load(f)
     except (OSError, ValueError):
         return None
@@ -593,7 +600,7 @@ def main() -> int:
             "frac": achieved / PEAK_HBM_GBPS,
             "traffic": traffic,
             "traffic_source": (f"rocprofv3 FETCH_SIZE and WRITE_SIZE runs committed in "
-                               f"{os.path.relpath(PMC_FILE, ROOT)}, taken on kernel source sha256 "
+                               f"{os.path.relpath(pmc_file(args.workload), ROOT)}, taken on kernel source sha256 "
                                f"{kernel_source_hash()[:16]}; not measured in this run")
             if traffic is not None else "null: no committed counter run matches this kernel source and workload",
         },

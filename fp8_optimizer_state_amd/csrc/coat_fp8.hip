@@ -717,45 +717,79 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t word, int half) {
     return (double)__builtin_bit_cast(float, half ? (word & 0xFFFF0000u) : (word << 16));
 }
 
-// Per-wave LDS area holding, after the element pass, the inputs that only the
-// exact requantization needs (raw codes and grads, dequantization constants),
-// so that no registers are held for them through the requantization.
+// Re-layout area of one wave for whole tiles. The global streams of a tile
+// are read and written 16 bytes per lane with consecutive lanes on
+// consecutive 16 bytes (a wave instruction covers 1 KB); measured on the
+// 13B list, the step's access pattern moves about 5 % faster that way than
+// with each lane reading and writing its own 16 elements (64 bytes of master
+// weights, 32 of grads and of the bf16 copy), which is the layout the
+// per-element work needs (a lane's elements lie in one group). So the grads
+// arrive 8 per lane per half tile, the master weights 4 per lane per quarter
+// tile, and the grads, the update term and the bf16 copy are re-laid between
+// the two layouts here: 256 chunks of 16 bytes, with one chunk of padding
+// after every 16 so that each of the lane patterns used hits 16 distinct
+// bank groups.
+constexpr int kXferChunks = 256 + 16;
+struct alignas(16) Xfer {
+    uint32_t w[kXferChunks * 4];
+};
+// byte offset of 16-byte chunk c of the tile's data
+__device__ __forceinline__ uint32_t xfer_off(uint32_t c) { return (c + (c >> 4)) * 16u; }
+// xfer_off(a + 16 j) = xfer_off(a) + 272 j; and for a group of four chunks
+// 4m .. 4m + 3 (never split by the padding) xfer_off(4m + q) = xfer_off(4m) + 16 q:
+// the per-lane part once, the rest as instruction offsets.
+constexpr uint32_t kXferRow = 17 * 16;
+// The lane's index, formed where it is used (two mbcnt instructions) and
+// opaque to the optimizer: offsets derived from it are then computed in each
+// tile rather than hoisted out of the tile loop into registers (spilled).
+__device__ __forceinline__ int lane_opaque() {
+    uint32_t l = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(l));
+    return (int)l;
+}
+
+// Per-wave LDS area after the element pass: what the rare exact paths need,
+// so that no registers are held for it through the requantization. Whole
+// tiles re-lay through x; their rare paths read the codes and grads again
+// from global memory (both unchanged until the tile's codes are stored).
+// Tiles that end inside their tensor park codes and grads here instead.
 struct ParkDirect {
-    uint32_t gw[8][kWave];
-    uint32_t mq[4][kWave];
-    uint32_t vq[4][kWave];
-    double og[6][kWave];  // m: a, a_lo, r; v: a, a_lo, r
+    union {
+        struct {
+            uint32_t gw[8][kWave];
+            uint32_t mq[4][kWave];
+            uint32_t vq[4][kWave];
+        } in;
+        Xfer x;
+    };
+    uint16_t wide[kWave];  // per lane: elements whose final master weight is in x (rare)
+    double og[6][kWave];   // m: a, a_lo, r; v: a, a_lo, r
 };
 struct ParkTab {
-    uint32_t gw[8][kWave];
-    uint32_t mq[4][kWave];
-    uint32_t vq[4][kWave];
+    Xfer x;
+    uint16_t wide[kWave];
     double s[kWave];      // the stored scale and exponent as loaded (the lane's moment, TileIn s0,
     float k[kWave];       // k0), from which the rare paths recompute the group constants
 };
 
 // Exact decision for the elements whose fast code is flagged in `amb` (one
 // moment): the element's new moment is recomputed in fp64 exactly as in the
-// main pass (its old code, grad and the dequantization constants read back
-// from the park area; `old` is the moment's code rows, og the moment's
-// dequantization constants), then rounded with the fp64 threshold (or from scratch for
+// main pass (its old code word old_word(w) and grad word grad_word(w), og the
+// moment's dequantization constants), then rounded with the fp64 threshold (or from scratch for
 // groups outside the fp32 path's range). Loops until no lane has a flagged
 // element.
-template <int F, typename PK, typename L>
-__device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&codes)[4],
-                                               const uint32_t (*old)[kWave], const PK& pk, const OldGroup& og,
-                                               const NewGroup& ng, const L& lq, const double* lqm,
+template <int F, typename OW, typename GW, typename L>
+__device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&codes)[4], OW old_word, GW grad_word,
+                                               const OldGroup& og, const NewGroup& ng, const L& lq, const double* lqm,
                                                const FmtRT& F_, double cb, bool square, CoefPtr cf) {
-    const int lane = threadIdx.x & (kWave - 1);
     while (__any((amb[0] | amb[1] | amb[2] | amb[3]) != 0u)) {
         if ((amb[0] | amb[1] | amb[2] | amb[3]) != 0u) {
             const int wi = amb[0] ? 0 : (amb[1] ? 1 : (amb[2] ? 2 : 3));
             const uint32_t aw = select4(wi, amb[0], amb[1], amb[2], amb[3]);
             const int bi = __builtin_ctz(aw) >> 3;
             const int e = 4 * wi + bi;
-            const uint32_t oldw = old[wi][lane];
-            const uint32_t gword = pk.gw[e >> 1][lane];
-            const double g = bf16_to_f64(gword, e & 1);
+            const uint32_t oldw = old_word(wi);
+            const double g = bf16_to_f64(grad_word(e >> 1), e & 1);
             double tb;
             const double mag = dequant_mag(oldw >> (8 * bi), 0, og, lq, tb);
             const double x = __builtin_fma(tb, mag, cb * (square ? g * g : g));
@@ -789,6 +823,11 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
 }
 
 // Inputs of one wavefront tile.
+// One tile's inputs in registers. Tiles that end inside their tensor: the
+// lane's own 16 elements throughout. Whole tiles (load_full_tile): codes and
+// the stored state as above, the grads 8 per lane per half tile (elements
+// 512 h + 8 lane + j) and the master weights 4 per lane per quarter tile
+// (elements 256 i + 4 lane + j, p[4 i + j]).
 struct TileIn {
     float p[16];
     uint32_t gw[8], mq[4], vq[4];
@@ -875,14 +914,21 @@ __device__ __forceinline__ void load_full_tile(const TensorRef& t, int64_t tile,
     in.mq[0] = a.x; in.mq[1] = a.y; in.mq[2] = a.z; in.mq[3] = a.w;
     const u32x4 b = *reinterpret_cast<const gu32x4*>(gp(t.vq) + e0);
     in.vq[0] = b.x; in.vq[1] = b.y; in.vq[2] = b.z; in.vq[3] = b.w;
+    // Grads 8 per lane per half tile, master weights 4 per lane per quarter
+    // tile, each wave load covering 1 KB (re-laid in step_tile). A grads load
+    // h puts chunk c = 64 h + 2 (lane mod 32) + lane / 32 (elements 8c ..
+    // 8c + 7) in the lane, so that one swap of the two halves' words between
+    // lanes l and l + 32 leaves each lane its own 16 elements.
+    const gu16* Gl = gp(t.g) + tile * kTile + (uint32_t)(16 * (lane & 31) + 8 * (lane >> 5));
+    const gfloat* Pl = gp(t.p) + tile * kTile + (uint32_t)(4 * lane);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const u32x4 v = reinterpret_cast<const gu32x4*>(gp(t.g) + e0)[i];
-        in.gw[4 * i] = v.x; in.gw[4 * i + 1] = v.y; in.gw[4 * i + 2] = v.z; in.gw[4 * i + 3] = v.w;
+    for (int h = 0; h < 2; ++h) {
+        const u32x4 v = *reinterpret_cast<const gu32x4*>(Gl + 512 * h);
+        in.gw[4 * h] = v.x; in.gw[4 * h + 1] = v.y; in.gw[4 * h + 2] = v.z; in.gw[4 * h + 3] = v.w;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const f32x4 v = reinterpret_cast<const gf32x4*>(gp(t.p) + e0)[i];
+        const f32x4 v = *reinterpret_cast<const gf32x4*>(Pl + 256 * i);
         in.p[4 * i] = v.x; in.p[4 * i + 1] = v.y; in.p[4 * i + 2] = v.z; in.p[4 * i + 3] = v.w;
     }
     // every load is issued before any use of what they return
@@ -1023,6 +1069,88 @@ __device__ __forceinline__ EntryPair table_entries(uint32_t e, const GroupTable&
 __device__ __forceinline__ LqSigned lq_source(const DirectTables& ct, int f, double) { return LqSigned{ct.lqb[f]}; }
 __device__ __forceinline__ LqSplit lq_source(const TabTables& ct, int f, double b) { return LqSplit{ct.lq[f], b}; }
 
+// The dequantization constants of both moments from the park area (rare
+// paths, after the element pass). Table path: each lane parked the stored
+// scale and exponent of moment (lane >> 2) & 1, lane i and lane 7 - i of each
+// 8 the two; direct path: both moments' constants.
+template <int FM, int FV, bool TAB, typename PK>
+__device__ __forceinline__ void parked_old_groups(const PK& pk, OldGroup& gm, OldGroup& gv) {
+    const int lane = threadIdx.x & (kWave - 1);
+    if constexpr (TAB) {
+        const FmtRT fm = fmt_rt<FM>(), fv = fmt_rt<FV>();
+        const bool q_odd = ((lane >> 2) & 1) != 0;
+        const OldGroup mine = old_group(pk.s[lane], pk.k[lane], q_odd ? fv.log2_fpmax : fm.log2_fpmax,
+                                        q_odd ? fv.log2_fpmax_lo : fm.log2_fpmax_lo);
+        const OldGroup other{xlane64(mine.a, 4), xlane64(mine.a_lo, 4), xlane64(mine.r, 4), xlane64(mine.r_lo, 4)};
+        gm = q_odd ? other : mine;
+        gv = q_odd ? mine : other;
+    } else {
+        gm = OldGroup{pk.og[0][lane], pk.og[1][lane], pk.og[2][lane], 0.0};
+        gv = OldGroup{pk.og[3][lane], pk.og[4][lane], pk.og[5][lane], 0.0};
+    }
+}
+
+// The rare exact statistics of a tile (some lane of the wave has a zero or a
+// non-finite new moment): zeros excluded from the minimum, non-finite moments
+// flagged, each element recomputed in fp64 from its code and grad words
+// (code_word(second, w), grad_word(w)). Moments finite in fp64 but beyond the
+// fp32 range (a bf16 grad of about 1e20 or more, or a huge stored state) leave
+// the fp32 update without a usable value: it is redone in fp64 from the
+// master weight as loaded (p0(i), before the tile's master weights are
+// stored), one element per lane at a time, and handed to on_wide(i, p').
+struct RareStats {
+    double amax_m, amin_m, amax_v, amin_v;
+    uint32_t bad;       // bit 0: a first moment of the lane is not finite, bit 1: a second moment
+    uint32_t redone;    // the lane's elements whose update was redone in fp64
+    uint32_t any_wide;  // some lane of the wave redid one
+};
+template <typename LQ, typename CW, typename GW, typename P0, typename OW>
+__device__ __forceinline__ RareStats rare_stats(const OldGroup& pm, const OldGroup& pv, const LQ& lq_m,
+                                                const LQ& lq_v, const StepConsts& c, int nvalid, CW code_word,
+                                                GW grad_word, P0 p0, OW on_wide) {
+    RareStats r{0.0, __builtin_inf(), 0.0, __builtin_inf(), 0u, 0u, 0u};
+    uint32_t wide = 0u;
+    // not unrolled: one element's code and grad words at a time
+#pragma unroll 1
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t wm = code_word(false, i >> 2);
+        const uint32_t wv = code_word(true, i >> 2);
+        const double g = bf16_to_f64(grad_word(i >> 1), i & 1);
+        double tbm, tbv;
+        const double m0 = dequant_mag(wm >> (8 * (i & 3)), 0, pm, lq_m, tbm);
+        const double v0 = dequant_mag(wv >> (8 * (i & 3)), 0, pv, lq_v, tbv);
+        const double m1 = __builtin_fma(tbm, m0, c.c1 * g);
+        const double v1 = __builtin_fma(tbv, v0, c.c2 * (g * g));
+        const double am = __builtin_fabs(m1), av = __builtin_fabs(v1);
+        const bool fin_m = am < __builtin_inf(), fin_v = av < __builtin_inf();
+        r.bad |= (fin_m ? 0u : 1u) | (fin_v ? 0u : 2u);
+        r.amax_m = vmax(r.amax_m, am);
+        r.amin_m = vmin(r.amin_m, am == 0.0 ? __builtin_inf() : am);
+        r.amax_v = vmax(r.amax_v, av);
+        r.amin_v = vmin(r.amin_v, av == 0.0 ? __builtin_inf() : av);
+        const bool beyond = !(__builtin_fabsf((float)m1) <= 0x1.fffffep+127f) ||
+                            !(__builtin_fabsf((float)v1) <= 0x1.fffffep+127f);
+        wide |= (beyond && fin_m && fin_v && i < nvalid) ? 1u << i : 0u;
+    }
+    r.any_wide = __any(wide != 0u) ? 1u : 0u;
+    while (__any(wide != 0u)) {
+        if (wide != 0u) {
+            const int i = __builtin_ctz(wide);
+            wide &= wide - 1u;
+            r.redone |= 1u << i;
+            const double g = bf16_to_f64(grad_word(i >> 1), i & 1);
+            double tbm, tbv;
+            const double m0 = dequant_mag(code_word(false, i >> 2) >> (8 * (i & 3)), 0, pm, lq_m, tbm);
+            const double v0 = dequant_mag(code_word(true, i >> 2) >> (8 * (i & 3)), 0, pv, lq_v, tbv);
+            const double m1 = __builtin_fma(tbm, m0, c.c1 * g);
+            const double v1 = __builtin_fma(tbv, v0, c.c2 * (g * g));
+            const double den = __builtin_sqrt(v1) * (double)c.ib2 + (double)c.eps;
+            on_wide(i, (float)((double)p0(i) * (double)c.decay - (double)c.ssz * (m1 / den)));
+        }
+    }
+    return r;
+}
+
 template <int FM, int FV, bool FULL, bool TAB, int LG>
 __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
                                           const typename StepLds<TAB>::Tables& ct,
@@ -1053,9 +1181,11 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     gu8* MQ = gp(t.mq);
     gu8* VQ = gp(t.vq);
     float (&p)[16] = in.p;
-    const uint32_t (&gw)[8] = in.gw;
+    uint32_t (&gw)[8] = in.gw;
     const uint32_t (&mq)[4] = in.mq;
     const uint32_t (&vq)[4] = in.vq;
+    // whole tiles: the wave's re-layout area
+    unsigned char* X = reinterpret_cast<unsigned char*>(&wl.pk.x);
 
     // ---- stored group state -> dequantization constants (all lanes must be
     // active: the pair split exchanges results between lanes)
@@ -1078,19 +1208,25 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
         return old_group(s0, k0, q_odd ? fv.log2_fpmax : fm.log2_fpmax, q_odd ? fv.log2_fpmax_lo : fm.log2_fpmax_lo);
     };
     // the same from the parked state (rare paths, after the element pass)
-    auto parked_groups = [&](OldGroup& gm, OldGroup& gv) {
-        if constexpr (TAB) {
-            const OldGroup mine = own_group(pk.s[lane], pk.k[lane]);
-            const OldGroup other{xlane64(mine.a, 4), xlane64(mine.a_lo, 4), xlane64(mine.r, 4), xlane64(mine.r_lo, 4)};
-            gm = q_odd ? other : mine;
-            gv = q_odd ? mine : other;
-        } else {
-            gm = OldGroup{pk.og[0][lane], pk.og[1][lane], pk.og[2][lane], 0.0};
-            gv = OldGroup{pk.og[3][lane], pk.og[4][lane], pk.og[5][lane], 0.0};
-        }
-    };
+    auto parked_groups = [&](OldGroup& gm, OldGroup& gv) { parked_old_groups<FM, FV, TAB>(pk, gm, gv); };
     OldGroup om, ov;
     if constexpr (!TAB) groups_of(in.s0, in.k0, in.s1, in.k1, om, ov);
+    // Whole tiles: the grads as loaded hold chunks 2 l and 2 l + 1 of the
+    // lane's half of the tile (l = lane mod 32) split between lanes l and
+    // l + 32 (lane l: its own even chunk and, in the second half's words, lane
+    // l + 32's even chunk; lane l + 32 the odd ones); one swap of lane l's
+    // second words with lane l + 32's first words (v_permlane32_swap) gives
+    // each lane its own 16 elements in order. Done just before the element pass.
+    auto own_grads = [&]() {
+        if constexpr (FULL) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const auto r = __builtin_amdgcn_permlane32_swap(gw[k], gw[4 + k], false, false);
+                gw[k] = r[0];
+                gw[4 + k] = r[1];
+            }
+        }
+    };
 
     // ---- per element: dequantize, moments, statistics, AdamW update
     const auto lq_m = lq_source(ct, 0, c.b1);
@@ -1115,11 +1251,30 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
             fin = __builtin_fmaf(xm[i], xv[i], fin);
         }
         // the master weights last: their loads were issued last
+        if constexpr (FULL) {
+            // whole tiles: the update term m / (sqrt(v) / (1 - b2^t)^(1/2) + eps)
+            // of the lane's elements into the re-layout area (chunks 4 lane + q),
+            // applied to the master weights in their layout after the rare paths
+            asm volatile("" ::: "memory");  // after the last table read (the area overlaps the tables)
+            const uint32_t ob = xfer_off(4 * lane_opaque());
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(xv[i]), c.ib2, c.eps);
-            const float upd = xm[i] * __builtin_amdgcn_rcpf(den);
-            p[i] = __builtin_fmaf(-c.ssz, upd, p[i] * c.decay);
+            for (int q = 0; q < 4; ++q) {
+                float u[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = 4 * q + j;
+                    const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(xv[i]), c.ib2, c.eps);
+                    u[j] = xm[i] * __builtin_amdgcn_rcpf(den);
+                }
+                *reinterpret_cast<f32x4*>(X + ob + 16 * q) = f32x4{u[0], u[1], u[2], u[3]};
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float den = __builtin_fmaf(__builtin_amdgcn_sqrtf(xv[i]), c.ib2, c.eps);
+                const float upd = xm[i] * __builtin_amdgcn_rcpf(den);
+                p[i] = __builtin_fmaf(-c.ssz, upd, p[i] * c.decay);
+            }
         }
     };
     if constexpr (TAB) {
@@ -1133,6 +1288,7 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
         // lookup overlap (the pass is otherwise bound by LDS latency; about
         // 1.5 % off the step on the 13B list).
         uint32_t em = code_offsets(mq[0], 0, ct.lut[0]), ev = code_offsets(vq[0], 0, ct.lut[1]);
+        own_grads();
         element_pass([&](int i, double cg, double cg2, double& m1, double& v1) {
             const EntryPair xm_ = table_entries(em, tm), xv_ = table_entries(ev, tv);
             if (i + 1 < kLaneElems) {
@@ -1144,6 +1300,7 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
         });
         asm volatile("" ::: "memory");  // the park area reuses the tables' LDS
     } else {
+        own_grads();
         element_pass([&](int i, double cg, double cg2, double& m1, double& v1) {
             double tbm, tbv;
             const double m0 = dequant_mag(mq[i >> 2], i & 3, om, lq_m, tbm);
@@ -1156,10 +1313,12 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     // the statistics are redone exactly.
     const bool special = amin_m == 0.0 || amin_v == 0.0 || !(__builtin_fabsf(fin) <= 0x1.fffffep+127f);
     // ---- park what only the exact paths (statistics with zeros, requantization) need
+    if constexpr (!FULL) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pk.gw[i][lane] = gw[i];
+        for (int i = 0; i < 8; ++i) pk.in.gw[i][lane] = gw[i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { pk.mq[i][lane] = mq[i]; pk.vq[i][lane] = vq[i]; }
+        for (int i = 0; i < 4; ++i) { pk.in.mq[i][lane] = mq[i]; pk.in.vq[i][lane] = vq[i]; }
+    }
     if constexpr (TAB) {
         pk.s[lane] = in.s0;
         pk.k[lane] = in.k0;
@@ -1169,76 +1328,106 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     }
     // later reads of the park area must come from LDS, not from registers
     asm volatile("" ::: "memory");
+    // The rare paths' codes and grads: whole tiles read them again from global
+    // memory (unchanged until this tile's codes are stored), others from the park area.
+    // (tile base, uniform, plus a 32-bit lane offset: one address register)
+    auto code_word = [&](bool second, int w) -> uint32_t {
+        if constexpr (FULL) {
+            const gu8* base = (second ? VQ : MQ) + tile * kTile;
+            return *reinterpret_cast<const gu32*>(base + (uint32_t)(16 * lane + 4 * w));
+        } else {
+            return second ? pk.in.vq[w][lane] : pk.in.mq[w][lane];
+        }
+    };
+    auto grad_word = [&](int w) -> uint32_t {
+        if constexpr (FULL) {
+            const gu16* base = gp(t.g) + tile * kTile;
+            return *reinterpret_cast<const gu32*>(base + (uint32_t)(16 * lane + 2 * w));
+        } else {
+            return pk.in.gw[w][lane];
+        }
+    };
 
     // bit 0: a first moment of the lane is not finite, bit 1: a second moment
     uint32_t bad = 0u;
-    // bit i: element i's moments are finite in fp64 but one lies beyond the
-    // fp32 range, so its update is redone in fp64
-    uint32_t wide = 0u;
-    if (__any(special)) {
-        // Rare: exact statistics with zeros excluded from the minimum and
-        // non-finite moments flagged, from the parked inputs.
+    // whole tiles: some lane's update was redone in fp64 (its final master
+    // weights are in the re-layout area, flagged in pk.wide)
+    bool any_wide = false;
+    if (__builtin_expect(__any(special), 0)) {
+        RareStats r;
         OldGroup pm, pv;
         parked_groups(pm, pv);
-        amax_m = 0.0; amin_m = __builtin_inf(); amax_v = 0.0; amin_v = __builtin_inf();
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t wm = pk.mq[i >> 2][lane];
-            const uint32_t wv = pk.vq[i >> 2][lane];
-            const double g = bf16_to_f64(pk.gw[i >> 1][lane], i & 1);
-            double tbm, tbv;
-            const double m0 = dequant_mag(wm >> (8 * (i & 3)), 0, pm, lq_m, tbm);
-            const double v0 = dequant_mag(wv >> (8 * (i & 3)), 0, pv, lq_v, tbv);
-            const double m1 = __builtin_fma(tbm, m0, c.c1 * g);
-            const double v1 = __builtin_fma(tbv, v0, c.c2 * (g * g));
-            const double am = __builtin_fabs(m1), av = __builtin_fabs(v1);
-            const bool fin_m = am < __builtin_inf(), fin_v = av < __builtin_inf();
-            bad |= (fin_m ? 0u : 1u) | (fin_v ? 0u : 2u);
-            amax_m = vmax(amax_m, am);
-            amin_m = vmin(amin_m, am == 0.0 ? __builtin_inf() : am);
-            amax_v = vmax(amax_v, av);
-            amin_v = vmin(amin_v, av == 0.0 ? __builtin_inf() : av);
-            const bool beyond = !(__builtin_fabsf((float)m1) <= 0x1.fffffep+127f) ||
-                                !(__builtin_fabsf((float)v1) <= 0x1.fffffep+127f);
-            wide |= (beyond && fin_m && fin_v && i < nvalid) ? 1u << i : 0u;
-        }
-        // Moments finite in fp64 but beyond the fp32 range (a bf16 grad of
-        // about 1e20 or more, or a huge stored state) leave the fp32 update
-        // without a usable value: it is redone in fp64 from the master weight
-        // as loaded (stored only after this point), one element per lane at a
-        // time, the result placed with a fixed-index select so that p stays in
-        // registers.
-        while (__any(wide != 0u)) {
-            if (wide != 0u) {
-                const int i = __builtin_ctz(wide);
-                wide &= wide - 1u;
-                const double g = bf16_to_f64(pk.gw[i >> 1][lane], i & 1);
-                double tbm, tbv;
-                const double m0 = dequant_mag(pk.mq[i >> 2][lane] >> (8 * (i & 3)), 0, pm, lq_m, tbm);
-                const double v0 = dequant_mag(pk.vq[i >> 2][lane] >> (8 * (i & 3)), 0, pv, lq_v, tbv);
-                const double m1 = __builtin_fma(tbm, m0, c.c1 * g);
-                const double v1 = __builtin_fma(tbv, v0, c.c2 * (g * g));
-                const double p0 = (double)P[e0 + i];
-                const double den = __builtin_sqrt(v1) * (double)c.ib2 + (double)c.eps;
-                const float pc = (float)(p0 * (double)c.decay - (double)c.ssz * (m1 / den));
+        if constexpr (FULL) {
+            r = rare_stats(pm, pv, lq_m, lq_v, c, nvalid, code_word, grad_word,
+                           [&](int i) { return (P + tile * kTile)[(uint32_t)(16 * lane + i)]; },
+                           [&](int i, float pc) {
+                               *reinterpret_cast<float*>(X + xfer_off(4 * lane_opaque() + (i >> 2)) + 4 * (i & 3)) = pc;
+                           });
+            if (r.any_wide) pk.wide[lane] = (uint16_t)r.redone;
+        } else {
+            r = rare_stats(pm, pv, lq_m, lq_v, c, nvalid, code_word, grad_word,
+                           [&](int i) { return P[e0 + i]; },
+                           [&](int i, float pc) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) p[j] = (j == i) ? pc : p[j];
-            }
+                               for (int j = 0; j < 16; ++j) p[j] = (j == i) ? pc : p[j];
+                           });
         }
+        amax_m = r.amax_m; amin_m = r.amin_m; amax_v = r.amax_v; amin_v = r.amin_v;
+        bad = r.bad;
+        any_wide = r.any_wide != 0u;
     }
 
     // ---- store the new master weights and the bf16 copy
-    if (nvalid == kLaneElems) {
+    if constexpr (FULL) {
+        // The update term to the master weights' layout (chunk 64 i + lane:
+        // elements 256 i + 4 lane + j), applied there; redone elements take
+        // their final value from the same slot.
+        const int xl = lane_opaque();
+        float pn[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 u = *reinterpret_cast<const f32x4*>(X + xfer_off(xl) + 4 * kXferRow * i);
+            const float uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pn[4 * i + j] = __builtin_fmaf(-c.ssz, uu[j], p[4 * i + j] * c.decay);
+            if (__builtin_expect(any_wide, 0)) {
+                // element 256 i + 4 lane + j lies in lane 16 i + lane / 4, at its index 4 (lane & 3) + j
+                const uint32_t fl = (pk.wide[16 * i + (xl >> 2)] >> (4 * (xl & 3))) & 0xFu;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if ((fl >> j) & 1u) pn[4 * i + j] = uu[j];
+            }
+        }
+        gfloat* Pl = P + tile * kTile + (uint32_t)(4 * xl);  // then constant offsets
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<gf32x4*>(Pl + 256 * i) = f32x4{pn[4 * i], pn[4 * i + 1], pn[4 * i + 2], pn[4 * i + 3]};
+        if (t.w) {
+            // bf16 pairs (one packed RNE convert each) to the grads' layout:
+            // elements 256 i + 4 lane .. + 3 are bytes 512 i + 8 lane .. + 7 of
+            // the copy, read back 16 bytes per lane (elements 512 h + 8 lane ..)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{pn[4 * i], pn[4 * i + 1]}, bf16x2));
+                const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{pn[4 * i + 2], pn[4 * i + 3]}, bf16x2));
+                *reinterpret_cast<u32x2*>(X + xfer_off(xl >> 1) + 8 * (xl & 1) + 2 * kXferRow * i) = u32x2{lo, hi};
+            }
+            gu16* Wl = gp(t.w) + tile * kTile + (uint32_t)(8 * xl);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                *reinterpret_cast<gu32x4*>(Wl + 512 * h) =
+                    *reinterpret_cast<const u32x4*>(X + xfer_off(xl) + 4 * kXferRow * h);
+        }
+    } else if (nvalid == kLaneElems) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             reinterpret_cast<gf32x4*>(P + e0)[i] = f32x4{p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]};
         if (t.w) {
+            // one packed RNE convert per pair (v_cvt_pk_bf16_f32)
             uint32_t wb[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const __bf16 lo = (__bf16)p[2 * i], hi = (__bf16)p[2 * i + 1];
-                wb[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-            }
+            for (int i = 0; i < 8; ++i)
+                wb[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p[2 * i], p[2 * i + 1]}, bf16x2));
             gu32x4* wp = reinterpret_cast<gu32x4*>(gp(t.w) + e0);
             wp[0] = u32x4{wb[0], wb[1], wb[2], wb[3]};
             wp[1] = u32x4{wb[4], wb[5], wb[6], wb[7]};
@@ -1350,8 +1539,10 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
         }
         OldGroup pm, pv;
         parked_groups(pm, pv);
-        redo_ambiguous<FM>(am, cm, pk.mq, pk, pm, nm, lq_m, ct.lqm[0], fm, c.c1, false, cf);
-        redo_ambiguous<FV>(av, cv, pk.vq, pk, pv, nv, lq_v, ct.lqm[1], fv, c.c2, true, cf);
+        redo_ambiguous<FM>(am, cm, [&](int w) { return code_word(false, w); }, grad_word, pm, nm, lq_m, ct.lqm[0],
+                           fm, c.c1, false, cf);
+        redo_ambiguous<FV>(av, cv, [&](int w) { return code_word(true, w); }, grad_word, pv, nv, lq_v, ct.lqm[1],
+                           fv, c.c2, true, cf);
     }
     if (any_flagged) {
         if (nm.flags & kPoison) { cm[0] = cm[1] = cm[2] = cm[3] = 0x7F7F7F7Fu; }
@@ -1598,6 +1789,30 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
     }
 }
 
+// 2^f on [-1/2, 1/2] to a relative error below 2^-28.5: the degree-6
+// polynomial interpolating 2^f at the seven Chebyshev nodes of the interval,
+// highest degree first. Used where the result is rounded to fp32 (the state
+// dequantizer), so that the rounded value is within one fp32 ulp.
+constexpr int kExp2ShortN = 7;
+__device__ constexpr double kExp2ShortC[kExp2ShortN] = {
+    0x1.443fffc87faa0p-13, 0x1.5f48c04f4eff9p-10, 0x1.3b2a1b7152d23p-7, 0x1.c6aecc669b99bp-5,
+    0x1.ebfbe045f4d57p-3,  0x1.62e430d034700p-1,  1.0};
+
+// Byte i of code word w dequantized and rounded to fp32:
+// sign(q) 2^(LQ[q] r + a + a_lo) (the sign from the code's sign bit, so that a
+// zero keeps it and a NaN stays NaN).
+__device__ __forceinline__ float dequant_f32(uint32_t w, int i, const OldGroup& og, const LqEntry* t) {
+    const uint32_t c = (w >> (8 * i)) & 0xFFu;
+    const double u = __builtin_fma(t[c].lq, og.r, og.a);
+    const double n = __builtin_rint(u);
+    const double f = (u - n) + og.a_lo;
+    double p = kExp2ShortC[0];
+#pragma unroll
+    for (int j = 1; j < kExp2ShortN; ++j) p = fma3(p, f, kExp2ShortC[j]);
+    const float mag = (float)__builtin_amdgcn_ldexp(p, cvt_i32_sat(n));
+    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, mag) | ((c & 0x80u) << 24));
+}
+
 template <int F>
 __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __restrict__ q,
                                                             const double* __restrict__ s,
@@ -1622,22 +1837,14 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __res
             const uint32_t w[4] = {a.x, a.y, a.z, a.w};
             float out[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                double tb;
-                const double mag = dequant_mag(w[i >> 2], i & 3, og, LqSigned{ct.lqb[0]}, tb);
-                out[i] = (float)(tb * mag);
-            }
+            for (int i = 0; i < 16; ++i) out[i] = dequant_f32(w[i >> 2], i & 3, og, ct.lqb[0]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 reinterpret_cast<gf32x4*>(X + e0)[i] = f32x4{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (i < nvalid) {
-                    double tb;
-                    const double mag = dequant_mag(Q[e0 + i], 0, og, LqSigned{ct.lqb[0]}, tb);
-                    X[e0 + i] = (float)(tb * mag);
-                }
+                if (i < nvalid) X[e0 + i] = dequant_f32(Q[e0 + i], 0, og, ct.lqb[0]);
         }
     }
 }

@@ -195,8 +195,9 @@ int coat_fp8_quantize(const float* x, int64_t n, int32_t group, int32_t fmt, uin
                       double* s, float* k, coat_stream_t stream);
 
 /*
- * Dequantize FP8 state to fp32: x = RN32(sign(q) (|q| s)^(1/k)), the value the
- * step starts from (in fp64) rounded to fp32. Used to export state.
+ * Dequantize FP8 state to fp32: x = sign(q) (|q| s)^(1/k), the value the step
+ * starts from (in fp64), to within one fp32 ulp (the power is evaluated to
+ * about 2^-28 before the rounding to fp32). Used to export state.
  */
 int coat_fp8_dequantize(const uint8_t* q, const double* s, const float* k, int64_t n,
                         int32_t group, int32_t fmt, float* x, coat_stream_t stream);

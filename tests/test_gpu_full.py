@@ -6,8 +6,11 @@ moments are quantized on the device for every group, then the parity sample's
 groups are overwritten with the oracle's own quantization of the same prior
 values, so that every input the oracle sees comes from the generator or the
 oracle. The sample (synth.parity_sample): every tensor's first and last group,
-every group of the first transformer block, and every 997th group.
+every group of the first transformer block, and every 997th group. An
+opt-in denser run (test_full_size_dense) takes every N-th group instead, N
+from the environment variable COAT_DENSE_PARITY (e.g. 97).
 """
+import os
 import time
 from concurrent.futures import ThreadPoolExecutor
 
@@ -107,13 +110,14 @@ def concat(lst):
     return {k: np.concatenate([d[k] for d in lst]) for k in lst[0]}
 
 
-@pytest.mark.parametrize("name", ["llama13b", "llama7b", "llama13b_g32"])
-def test_full_size_sampled(coat, name):
+def run_full(coat, name, every=997):
+    """One planned step over the whole list; the sampled groups against the oracle."""
     wl = synth.WORKLOADS[name]
     dev = torch.device("cuda")
-    sample = synth.parity_sample(wl)
-    n_sample = sum(len(ix) for _, ix in sample) * wl.group
-    log(f"test_full_size_sampled {name}: {wl.n_params} params, sample {n_sample} params")
+    sample = synth.parity_sample(wl, every=every)
+    n_groups = sum(len(ix) for _, ix in sample)
+    log(f"{name}: {wl.n_params} params, sample every {every}th group: {n_groups} groups, "
+        f"{n_groups * wl.group} params")
     t0 = time.time()
     st, host = build(coat, wl, dev, sample)
     log(f"  inputs on device ({time.time() - t0:.1f} s)")
@@ -130,5 +134,24 @@ def test_full_size_sampled(coat, name):
     log(f"  gpu step done ({time.time() - t0:.1f} s)")
     ref = oracle_steps(host, wl, h["step"])
     log(f"  oracle done ({time.time() - t0:.1f} s)")
-    met = compare(concat(got), concat(ref), name)
+    g, r = concat(got), concat(ref)
+    met = compare(g, r, name)
+    for m in ("m", "v"):
+        log(f"  {m}: groups {len(g[m + 'k'])}, k identical in {int(np.sum(g[m + 'k'] == r[m + 'k']))}, "
+            f"k rel max {met[m + '_k_rel']:.3g}, s rel max {met[m + '_s_rel']:.3g}, "
+            f"codes differing {int(np.sum(g[m + 'q'] != r[m + 'q']))}")
+    return met
+
+
+@pytest.mark.parametrize("name", ["llama13b", "llama7b", "llama13b_g32"])
+def test_full_size_sampled(coat, name):
+    met = run_full(coat, name)
+    assert met["m_k_rel"] < 1e-6 and met["v_k_rel"] < 1e-6
+
+
+@pytest.mark.skipif(not os.environ.get("COAT_DENSE_PARITY"),
+                    reason="opt-in: COAT_DENSE_PARITY=<stride> samples every stride-th group (e.g. 97)")
+@pytest.mark.parametrize("name", ["llama13b", "llama7b", "llama13b_g32"])
+def test_full_size_dense(coat, name):
+    met = run_full(coat, name, every=int(os.environ["COAT_DENSE_PARITY"]))
     assert met["m_k_rel"] < 1e-6 and met["v_k_rel"] < 1e-6
