@@ -1696,7 +1696,9 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
                                                           int lg2_group, int expand, uint8_t* q,
                                                           double* s, float* k) {
     __shared__ DirectTables ct;
+    __shared__ Xfer xfs[kWavesPerBlock];
     fill_direct_tables<F, F>(ct, 1.0, 1.0);
+    unsigned char* XA = reinterpret_cast<unsigned char*>(&xfs[threadIdx.x / kWave]);
     const int64_t tiles = (n + kTile - 1) / kTile;
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1709,10 +1711,19 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const float* __restric
         const int64_t rem = n - e0;
         const int nvalid = rem <= 0 ? 0 : (rem >= kLaneElems ? kLaneElems : (int)rem);
         float xf[16];
-        if (nvalid == kLaneElems) {
+        if ((tile + 1) * kTile <= n) {
+            // a whole tile: loaded 4 elements per lane per quarter tile (each
+            // wave load 1 KB), re-laid through LDS to the lane's own 16
+            const int xl = lane_opaque();
+            const gfloat* Xl = X + tile * kTile + (uint32_t)(4 * xl);
+            const uint32_t ib = xfer_off(xl);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<f32x4*>(XA + ib + 4 * kXferRow * i) = *reinterpret_cast<const gf32x4*>(Xl + 256 * i);
+            const uint32_t ob = xfer_off(4 * lane_opaque());
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const f32x4 v = reinterpret_cast<const gf32x4*>(X + e0)[i];
+                const f32x4 v = *reinterpret_cast<const f32x4*>(XA + ob + 16 * i);
                 xf[4 * i] = v.x; xf[4 * i + 1] = v.y; xf[4 * i + 2] = v.z; xf[4 * i + 3] = v.w;
             }
         } else {
@@ -1799,11 +1810,11 @@ __device__ constexpr double kExp2ShortC[kExp2ShortN] = {
     0x1.ebfbe045f4d57p-3,  0x1.62e430d034700p-1,  1.0};
 
 // Byte i of code word w dequantized and rounded to fp32:
-// sign(q) 2^(LQ[q] r + a + a_lo) (the sign from the code's sign bit, so that a
-// zero keeps it and a NaN stays NaN).
-__device__ __forceinline__ float dequant_f32(uint32_t w, int i, const OldGroup& og, const LqEntry* t) {
+// sign(q) 2^(LQ[q] r + a + a_lo) (LQ of the magnitude from lq[128], the sign
+// from the code's sign bit, so that a zero keeps it and a NaN stays NaN).
+__device__ __forceinline__ float dequant_f32(uint32_t w, int i, const OldGroup& og, const double* lq) {
     const uint32_t c = (w >> (8 * i)) & 0xFFu;
-    const double u = __builtin_fma(t[c].lq, og.r, og.a);
+    const double u = __builtin_fma(lq[c & 0x7Fu], og.r, og.a);
     const double n = __builtin_rint(u);
     const double f = (u - n) + og.a_lo;
     double p = kExp2ShortC[0];
@@ -1818,8 +1829,11 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __res
                                                             const double* __restrict__ s,
                                                             const float* __restrict__ k, int64_t n,
                                                             int lg2_group, float* __restrict__ x) {
-    __shared__ DirectTables ct;
-    fill_direct_tables<F, F>(ct, 1.0, 1.0);
+    __shared__ double lq[128];
+    __shared__ Xfer xfs[kWavesPerBlock];
+    if (threadIdx.x < 128) lq[threadIdx.x] = lq_entry<F>((int)threadIdx.x);
+    __syncthreads();
+    unsigned char* XA = reinterpret_cast<unsigned char*>(&xfs[threadIdx.x / kWave]);
     const int64_t tiles = (n + kTile - 1) / kTile;
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1832,19 +1846,28 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __res
         if (nvalid == 0) continue;
         const int64_t gi = e0 >> lg2_group;
         const OldGroup og = old_group(gp(s)[gi], gp(k)[gi], Fmt<F>::LOG2_FPMAX, Fmt<F>::LOG2_FPMAX_LO);
-        if (nvalid == kLaneElems) {
+        if ((tile + 1) * kTile <= n) {
+            // a whole tile: the lane's 16 values re-laid through LDS and stored
+            // 4 per lane per quarter tile (each wave store 1 KB)
             const u32x4 a = *reinterpret_cast<const gu32x4*>(Q + e0);
             const uint32_t w[4] = {a.x, a.y, a.z, a.w};
             float out[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) out[i] = dequant_f32(w[i >> 2], i & 3, og, ct.lqb[0]);
+            for (int i = 0; i < 16; ++i) out[i] = dequant_f32(w[i >> 2], i & 3, og, lq);
+            const uint32_t ob = xfer_off(4 * lane_opaque());
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                reinterpret_cast<gf32x4*>(X + e0)[i] = f32x4{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
+                *reinterpret_cast<f32x4*>(XA + ob + 16 * i) = f32x4{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
+            const int xl = lane_opaque();
+            gfloat* Xl = X + tile * kTile + (uint32_t)(4 * xl);
+            const uint32_t ib = xfer_off(xl);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<gf32x4*>(Xl + 256 * i) = *reinterpret_cast<const f32x4*>(XA + ib + 4 * kXferRow * i);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (i < nvalid) X[e0 + i] = dequant_f32(Q[e0 + i], 0, og, ct.lqb[0]);
+                if (i < nvalid) X[e0 + i] = dequant_f32(Q[e0 + i], 0, og, lq);
         }
     }
 }
