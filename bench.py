@@ -337,7 +337,7 @@ def ceiling(args) -> int:
         raise RuntimeError(f"{path} is not built; run python -c 'import __graft_entry__ as g; g.build()'")
     probe = ctypes.CDLL(path)
     P = ctypes.c_void_p
-    probe.ceiling_pattern_pass.argtypes = [P] * 9 + [ctypes.c_int64, ctypes.c_int, ctypes.c_int, P]
+    probe.ceiling_pattern_pass.argtypes = [P] * 9 + [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P]
     probe.ceiling_pattern_pass.restype = ctypes.c_int
     probe.ceiling_copy_pass.argtypes = [P, P, ctypes.c_int64, P]
     probe.ceiling_read_pass.argtypes = [P, ctypes.c_int64, P, P]
@@ -361,10 +361,11 @@ def ceiling(args) -> int:
     bpp = wl.bytes_per_param()
     step_no = [h["step"]]
 
-    def probe_pass(lds):
+    def probe_pass(layout, lds):
         rc = probe.ceiling_pattern_pass(st.params.data_ptr(), st.params_bf16.data_ptr(), st.grads.data_ptr(),
                                         st.m_q.data_ptr(), st.v_q.data_ptr(), st.m_s.data_ptr(), st.m_k.data_ptr(),
-                                        st.v_s.data_ptr(), st.v_k.data_ptr(), n_probe, lg, lds, stream.cuda_stream)
+                                        st.v_s.data_ptr(), st.v_k.data_ptr(), n_probe, lg, layout, lds,
+                                        stream.cuda_stream)
         assert rc == 0, rc
 
     def step_once():
@@ -386,8 +387,10 @@ def ceiling(args) -> int:
              ("write 4 GiB", lambda: plain(probe.ceiling_write_pass(bufb.data_ptr(), n16, stream.cuda_stream)), gib4),
              ("copy 4 GiB (probe kernel)", lambda: plain(probe.ceiling_copy_pass(bufa.data_ptr(), bufb.data_ptr(), n16,
                                                                                stream.cuda_stream)), 2 * gib4),
-             ("pattern floor, step residency", lambda: probe_pass(step_lds), bpp * n_probe),
-             ("pattern floor, full residency", lambda: probe_pass(0), bpp * n_probe),
+             ("pattern floor, lane-contiguous, step residency", lambda: probe_pass(0, step_lds), bpp * n_probe),
+             ("pattern floor, whole-tile (the step's), step residency", lambda: probe_pass(1, step_lds),
+              bpp * n_probe),
+             ("pattern floor, whole-tile, full residency", lambda: probe_pass(1, 0), bpp * n_probe),
              ("step", step_once, bpp * wl.n_params))
     for _, fn, _ in kinds:
         for _ in range(args.warmup):
