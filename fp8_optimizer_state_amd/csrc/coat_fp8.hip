@@ -29,7 +29,6 @@
 //   * the multi-tensor kernel walks a descriptor table of a whole parameter
 //     list in one launch; tiles never span tensors.
 #include <mutex>
-#include <vector>
 
 #include "coat_common.h"
 
@@ -1986,14 +1985,15 @@ static __device__ __align__(256) unsigned char scratch[kStaticLayout.total];
 
 namespace {
 
-// The tables reach the array through kernel arguments (captured at launch, so
-// the host side needs no staging memory and no synchronization).
+// Plan tables reach device memory (the static array, or a caller's
+// workspace) through kernel arguments (captured at launch, so the host side
+// needs no staging memory and no synchronization).
 __global__ __launch_bounds__(64) void arg_copy_kernel(ArgChunk chunk, uint32_t bytes, unsigned char* dst) {
     for (uint32_t i = threadIdx.x * 16u; i < bytes; i += 64u * 16u)
         *reinterpret_cast<u32x4*>(dst + i) = *reinterpret_cast<const u32x4*>(chunk.data + i);
 }
 
-// ChunkWriter's sink for the device array: one copy launch per chunk.
+// ChunkWriter's sink for device memory at `base`: one copy launch per chunk.
 struct LaunchSink {
     unsigned char* base;
     hipStream_t st;
@@ -2073,14 +2073,13 @@ int coat_multi_plan_init(coat_multi_plan* plan, const coat_tensor* tensors, int3
     if (!plan || count < 0 || (count > 0 && !tensors)) return COAT_EINVAL;
     if (!workspace || workspace_bytes < coat_multi_workspace_bytes(count)) return COAT_EINVAL;
     if (!aligned(workspace, 256)) return COAT_EALIGN;
-    const size_t total = coat_multi_workspace_bytes(count);
-    std::vector<unsigned char> host(total);
     PlanSummary sum;
-    const int rc = fill_plan(tensors, count, host.data(), host.size(), &sum);
+    const int rc = scan_tensors(tensors, count, &sum);
     if (rc) return rc;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (hipMemcpyAsync(workspace, host.data(), total, hipMemcpyHostToDevice, st) != hipSuccess) return COAT_EHIP;
-    if (hipStreamSynchronize(st) != hipSuccess) return COAT_EHIP;
+    // the tables travel in the arguments of small copy launches on `stream`:
+    // no host staging buffer, no wait
+    LaunchSink sink{static_cast<unsigned char*>(workspace), reinterpret_cast<hipStream_t>(stream)};
+    if (!write_plan_tables(tensors, count, plan_layout((size_t)count), sink)) return COAT_EHIP;
     plan->workspace = workspace;
     plan->count = count;
     plan->tiles = sum.tiles;
@@ -2146,7 +2145,7 @@ int coat_fp8_adamw_step_multi_static(const coat_tensor* tensors, int32_t count, 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     // every byte the step reads is written here first; nothing needs clearing
     LaunchSink sink{ws, st};
-    if (!write_static_tables(tensors, count, sink)) return COAT_EHIP;
+    if (!write_plan_tables(tensors, count, kStaticLayout, sink)) return COAT_EHIP;
     const TensorRef* dts = reinterpret_cast<const TensorRef*>(ws + kStaticLayout.desc);
     const int64_t* dfb = reinterpret_cast<const int64_t*>(ws + kStaticLayout.fb);
     const int32_t* dpt = reinterpret_cast<const int32_t*>(ws + kStaticLayout.partial);

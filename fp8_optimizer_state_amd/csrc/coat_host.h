@@ -1,6 +1,7 @@
 // Host-side logic of the step library that touches no GPU: argument checks,
-// the step's constants, and the multi-tensor plan tables (the workspace image
-// and its chunked copy into the library's static device array). Plain C++
+// the step's constants, and the multi-tensor plan tables with their chunked
+// copy into device memory (a caller's workspace or the library's static
+// array). Plain C++
 // with no HIP dependency, so that the same code builds into a host-only
 // driver that runs under AddressSanitizer and UndefinedBehaviorSanitizer on
 // the CPU.
@@ -145,36 +146,12 @@ inline int scan_tensors(const coat_tensor* tensors, int32_t count, PlanSummary* 
     return COAT_OK;
 }
 
-// Writes the plan tables of `count` tensors into host memory `image` of
-// `image_bytes` (at least plan_layout(count).total; the padding is zeroed) and
-// sums the list. COAT_EINVAL if the image is too small, else scan_tensors' status.
-inline int fill_plan(const coat_tensor* tensors, int32_t count, void* image, size_t image_bytes, PlanSummary* s) {
-    if (count < 0 || (count > 0 && !tensors) || !image) return COAT_EINVAL;
-    const PlanLayout L = plan_layout((size_t)count);
-    if (image_bytes < L.total) return COAT_EINVAL;
-    const int rc = scan_tensors(tensors, count, s);
-    if (rc) return rc;
-    unsigned char* base = static_cast<unsigned char*>(image);
-    memset(base, 0, L.total);
-    if (count > 0) memcpy(base + L.desc, tensors, sizeof(TensorRef) * (size_t)count);
-    int64_t* fb = reinterpret_cast<int64_t*>(base + L.fb);
-    int32_t* partial = reinterpret_cast<int32_t*>(base + L.partial);
-    int64_t acc = 0;
-    int32_t np = 0;
-    for (int32_t i = 0; i < count; ++i) {
-        fb[i] = acc;
-        acc += tensors[i].n / kPlanTile;
-        if (tensors[i].n % kPlanTile) partial[np++] = i;
-    }
-    fb[count] = acc;
-    return COAT_OK;
-}
-
 // The static plan tables (coat_fp8_adamw_step_multi_static): the same sections
 // sized for COAT_STATIC_MAX_TENSORS tensors.
 constexpr PlanLayout kStaticLayout = plan_layout((size_t)COAT_STATIC_MAX_TENSORS);
 
-// The tables reach device memory through kernel arguments, 3 KB per copy.
+// The tables reach device memory (a caller's workspace or the library's
+// static array) through kernel arguments, 3 KB per copy.
 constexpr uint32_t kArgChunkBytes = 3072;
 struct alignas(16) ArgChunk {
     unsigned char data[kArgChunkBytes];
@@ -218,16 +195,20 @@ class ChunkWriter {
     bool ok_ = true;
 };
 
-// Every byte of the static tables that a step over `count` tensors reads,
-// through `sink`: descriptors [0, count), prefix [0, count], partial list
-// [0, n_partial). False if the sink failed. The caller has checked count
-// against COAT_STATIC_MAX_TENSORS and the descriptors (scan_tensors).
+// Every byte of the plan tables that a step over `count` tensors reads, in
+// the sections of layout L (plan_layout(count) for a caller's workspace,
+// kStaticLayout for the static array), through `sink`: descriptors
+// [0, count), the prefix of whole tiles [0, count] (first 0, last the total)
+// and the indices of the tensors whose last tile is partial [0, n_partial).
+// The 16-byte rounding of a chunk stays inside its 256-byte aligned section.
+// False if the sink failed. The caller has checked the descriptors
+// (scan_tensors) and that L holds `count` tensors.
 template <class Sink>
-bool write_static_tables(const coat_tensor* tensors, int32_t count, Sink& sink) {
-    ChunkWriter<Sink> desc(kStaticLayout.desc, sink);
+bool write_plan_tables(const coat_tensor* tensors, int32_t count, const PlanLayout& L, Sink& sink) {
+    ChunkWriter<Sink> desc(L.desc, sink);
     desc.put(tensors, sizeof(TensorRef) * (size_t)count);
     desc.flush();
-    ChunkWriter<Sink> fbw(kStaticLayout.fb, sink);
+    ChunkWriter<Sink> fbw(L.fb, sink);
     int64_t acc = 0;
     for (int32_t i = 0; i < count; ++i) {
         fbw.put(&acc, sizeof(acc));
@@ -235,7 +216,7 @@ bool write_static_tables(const coat_tensor* tensors, int32_t count, Sink& sink) 
     }
     fbw.put(&acc, sizeof(acc));
     fbw.flush();
-    ChunkWriter<Sink> pw(kStaticLayout.partial, sink);
+    ChunkWriter<Sink> pw(L.partial, sink);
     for (int32_t i = 0; i < count; ++i)
         if (tensors[i].n % kPlanTile) pw.put(&i, sizeof(i));
     pw.flush();

@@ -38,7 +38,8 @@
  *     boundary; s and k arrays need their natural alignment;
  *   - group G must be a power of two in [16, 1024];
  *   - return value: COAT_OK, or a negative status (see coat_strerror); on
- *     error nothing has been enqueued.
+ *     error nothing has been enqueued, except where COAT_EHIP is said to
+ *     leave earlier launches of the same call.
  */
 #ifndef COAT_FP8_H
 #define COAT_FP8_H
@@ -126,11 +127,16 @@ typedef struct coat_multi_plan {
 } coat_multi_plan;
 
 /*
- * Validate `count` descriptors (host array) and copy them, with a tile table,
- * into `workspace` (device memory, 256-byte aligned, at least
- * coat_multi_workspace_bytes(count) bytes). This set-up call waits for its copy
- * on `stream` to finish before returning. The plan stays valid while the
- * tensors' buffers and the workspace do.
+ * Validate `count` descriptors (host array) and enqueue on `stream` their copy,
+ * with a tile table, into `workspace` (device memory, 256-byte aligned, at
+ * least coat_multi_workspace_bytes(count) bytes). The tables travel in the
+ * arguments of a few small copy launches (about 3 KB each), so the call
+ * neither stages through host memory nor waits: it returns once they are
+ * enqueued, and the host array `tensors` is read during the call only. Steps
+ * enqueued after it on the same stream see the tables; a step on another
+ * stream must be ordered after them by the caller. The plan stays valid while
+ * the tensors' buffers and the workspace do. COAT_EHIP (a refused launch) may
+ * leave the copies before it enqueued.
  */
 int coat_multi_plan_init(coat_multi_plan* plan, const coat_tensor* tensors, int32_t count,
                          void* workspace, size_t workspace_bytes, coat_stream_t stream);
@@ -147,7 +153,8 @@ int coat_fp8_adamw_step_planned(const coat_multi_plan* plan, int32_t group, int3
 
 /*
  * Convenience: coat_multi_plan_init followed by coat_fp8_adamw_step_planned
- * (so it waits for the table copy, then enqueues the step).
+ * (it enqueues the table copies, then the step, all on `stream`, and returns
+ * without waiting).
  */
 int coat_fp8_adamw_step_multi(const coat_tensor* tensors, int32_t count, int32_t group,
                               int32_t fmt_m, int32_t fmt_v, float lr, float beta1, float beta2,

@@ -1,6 +1,6 @@
 // Drives the step library's host-side logic (coat_host.h: argument checks,
 // the step constants, the multi-tensor plan tables and their chunked copy
-// into the static table array) under AddressSanitizer and
+// into a workspace or the static table array) under AddressSanitizer and
 // UndefinedBehaviorSanitizer on the CPU (built by tests/test_host_sanitize.py).
 // Descriptor arrays and table images are heap-allocated at exactly the size a
 // call may touch, so any read or write past them is reported. Element
@@ -8,7 +8,7 @@
 // never dereferences them.
 //
 //   host_driver <sizes-file>            every check; prints "ok" at the end
-//   host_driver <sizes-file> overrun    fill_plan over one descriptor more
+//   host_driver <sizes-file> overrun    scan_tensors over one descriptor more
 //                                       than the array holds (must be reported)
 #include <math.h>
 #include <stdint.h>
@@ -135,66 +135,80 @@ static void check_tensors() {
     }
 }
 
-// The plan image of a list, checked field by field against a direct recount.
+// A sink that copies each chunk into a host image of exactly `cap` bytes
+// (the workspace or static array it stands for), rejecting a chunk that is
+// empty, oversized, unaligned or past the end.
+struct CopySink {
+    unsigned char* dst;
+    size_t cap;
+    int calls;
+    bool operator()(const ArgChunk& c, uint32_t bytes, size_t off) {
+        if (bytes == 0 || bytes > kArgChunkBytes || bytes % 16 || off % 16 || off + bytes > cap) return false;
+        memcpy(dst + off, c.data, bytes);
+        ++calls;
+        return true;
+    }
+};
+
+// The tables written in layout L, checked field by field against a direct
+// recount of the list.
+static void check_tables(const coat_tensor* ts, const std::vector<int64_t>& sizes, const PlanLayout& L) {
+    const int32_t count = (int32_t)sizes.size();
+    unsigned char* image = static_cast<unsigned char*>(malloc(L.total));
+    memset(image, 0xA5, L.total);
+    CopySink sink{image, L.total, 0};
+    CHECK(write_plan_tables(ts, count, L, sink));
+    CHECK(sink.calls >= 1);  // the prefix is written even for an empty list
+    const int64_t* fb = reinterpret_cast<const int64_t*>(image + L.fb);
+    const int32_t* part = reinterpret_cast<const int32_t*>(image + L.partial);
+    int64_t full = 0;
+    int32_t np = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        CHECK(memcmp(image + L.desc + sizeof(TensorRef) * (size_t)i, &ts[i], sizeof(TensorRef)) == 0);
+        CHECK(fb[i] == full);
+        full += sizes[(size_t)i] / 1024;
+        if (sizes[(size_t)i] % 1024) CHECK(part[np++] == i);
+    }
+    CHECK(fb[count] == full);
+    // a failing sink is reported
+    struct FailSink {
+        bool operator()(const ArgChunk&, uint32_t, size_t) { return false; }
+    } fail;
+    CHECK(!write_plan_tables(ts, count, L, fail));
+    free(image);
+}
+
+// The plan of a list: its summary and its tables in the workspace layout and,
+// when the list fits, in the static array's layout.
 static void check_plan(const std::vector<int64_t>& sizes) {
     const int32_t count = (int32_t)sizes.size();
     // exactly `count` descriptors on the heap (one allocation of that size)
     coat_tensor* ts = static_cast<coat_tensor*>(malloc(sizeof(coat_tensor) * (count ? count : 1)));
-    for (int32_t i = 0; i < count; ++i) ts[i] = fake_tensor(sizes[i], i);
+    for (int32_t i = 0; i < count; ++i) ts[i] = fake_tensor(sizes[(size_t)i], i);
     const PlanLayout L = plan_layout((size_t)count);
     CHECK(L.desc == 0 && L.fb % 256 == 0 && L.partial % 256 == 0 && L.total % 256 == 0);
     CHECK(L.fb >= sizeof(TensorRef) * (size_t)count && L.partial - L.fb >= 8 * ((size_t)count + 1));
-    unsigned char* image = static_cast<unsigned char*>(malloc(L.total));
+    CHECK(L.total - L.partial >= 4 * (size_t)count);
     PlanSummary s;
-    CHECK(fill_plan(ts, count, image, L.total - 1, &s) == COAT_EINVAL);  // one byte short
-    CHECK(fill_plan(ts, count, image, L.total, &s) == COAT_OK);
+    CHECK(scan_tensors(ts, count, &s) == COAT_OK);
     int64_t full = 0, tiles = 0, n_total = 0;
     int32_t np = 0;
-    const int64_t* fb = reinterpret_cast<const int64_t*>(image + L.fb);
-    const int32_t* part = reinterpret_cast<const int32_t*>(image + L.partial);
     for (int32_t i = 0; i < count; ++i) {
-        CHECK(memcmp(image + L.desc + sizeof(TensorRef) * (size_t)i, &ts[i], sizeof(TensorRef)) == 0);
-        CHECK(fb[i] == full);
-        full += sizes[i] / 1024;
-        tiles += (sizes[i] + 1023) / 1024;
-        n_total += sizes[i];
-        if (sizes[i] % 1024) CHECK(part[np++] == i);
+        full += sizes[(size_t)i] / 1024;
+        tiles += (sizes[(size_t)i] + 1023) / 1024;
+        n_total += sizes[(size_t)i];
+        np += sizes[(size_t)i] % 1024 ? 1 : 0;
     }
-    CHECK(fb[count] == full);
     CHECK(s.full == full && s.tiles == tiles && s.n_total == n_total && s.n_partial == np);
-    for (size_t b = L.partial + sizeof(int32_t) * (size_t)np; b < L.total; ++b) CHECK(image[b] == 0);
-
-    // the static tables through a sink that copies each chunk into an image of
-    // the static array's exact size: the sections the step reads equal the plan's
-    if (count <= COAT_STATIC_MAX_TENSORS) {
-        PlanSummary s2;
-        CHECK(scan_tensors(ts, count, &s2) == COAT_OK);
-        CHECK(s2.full == s.full && s2.tiles == s.tiles && s2.n_total == s.n_total && s2.n_partial == s.n_partial);
-        unsigned char* st = static_cast<unsigned char*>(malloc(kStaticLayout.total));
-        memset(st, 0xA5, kStaticLayout.total);
-        struct CopySink {
-            unsigned char* dst;
-            size_t cap;
-            int calls;
-            bool operator()(const ArgChunk& c, uint32_t bytes, size_t off) {
-                if (bytes == 0 || bytes > kArgChunkBytes || bytes % 16 || off % 16 || off + bytes > cap) return false;
-                memcpy(dst + off, c.data, bytes);
-                ++calls;
-                return true;
-            }
-        } sink{st, kStaticLayout.total, 0};
-        CHECK(write_static_tables(ts, count, sink));
-        CHECK(memcmp(st + kStaticLayout.desc, image + L.desc, sizeof(TensorRef) * (size_t)count) == 0);
-        CHECK(memcmp(st + kStaticLayout.fb, image + L.fb, sizeof(int64_t) * ((size_t)count + 1)) == 0);
-        CHECK(memcmp(st + kStaticLayout.partial, image + L.partial, sizeof(int32_t) * (size_t)np) == 0);
-        // a failing sink is reported
-        struct FailSink {
-            bool operator()(const ArgChunk&, uint32_t, size_t) { return false; }
-        } fail;
-        CHECK(!write_static_tables(ts, count, fail));
-        free(st);
+    check_tables(ts, sizes, L);
+    if (count <= COAT_STATIC_MAX_TENSORS) check_tables(ts, sizes, kStaticLayout);
+    // a bad descriptor anywhere in the list is found
+    if (count > 0) {
+        coat_tensor keep = ts[count - 1];
+        ts[count - 1] = with_field(keep, 2, 0);  // no grads
+        CHECK(scan_tensors(ts, count, &s) == (keep.n ? COAT_EINVAL : COAT_OK));
+        ts[count - 1] = keep;
     }
-    free(image);
     free(ts);
 }
 
@@ -229,12 +243,9 @@ int main(int argc, char** argv) {
         const int32_t count = (int32_t)model.size();
         coat_tensor* ts = static_cast<coat_tensor*>(malloc(sizeof(coat_tensor) * (size_t)(count - 1)));
         for (int32_t i = 0; i + 1 < count; ++i) ts[i] = fake_tensor(model[(size_t)i], i);
-        const PlanLayout L = plan_layout((size_t)count);
-        unsigned char* image = static_cast<unsigned char*>(malloc(L.total));
         PlanSummary s;
-        const int rc = fill_plan(ts, count, image, L.total, &s);
+        const int rc = scan_tensors(ts, count, &s);
         printf("not reported: rc %d\n", rc);
-        free(image);
         free(ts);
         return 0;
     }

@@ -1,6 +1,6 @@
 """The step library's host-side logic (fp8_optimizer_state_amd/csrc/coat_host.h:
 argument checks, step constants, multi-tensor plan tables and their chunked
-copy into the static table array) under AddressSanitizer and
+copy into a workspace or the static table array) under AddressSanitizer and
 UndefinedBehaviorSanitizer on the CPU. The same header is compiled into the
 library; here a C++ driver calls it with exactly-sized heap buffers on the
 Llama-2-13B list (363 tensors), ragged lists and a list filling the static
@@ -57,4 +57,4 @@ def test_planted_overrun_is_reported(driver):
     run = _run([exe, sizes, "overrun"])
     assert run.returncode != 0, run.stdout
     assert "heap-buffer-overflow" in run.stderr, run.stderr[-2000:]
-    assert "fill_plan" in run.stderr or "scan_tensors" in run.stderr
+    assert "scan_tensors" in run.stderr
