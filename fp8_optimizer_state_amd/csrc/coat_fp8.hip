@@ -10,14 +10,18 @@
 //
 // Design (MI355X / CDNA4):
 //   * one wavefront owns a tile of 1024 consecutive elements of one tensor;
-//     each lane owns 16 consecutive elements (128-bit loads and stores of
-//     every stream);
+//     for the per-element work each lane owns 16 consecutive elements (codes
+//     and per-group state are read and written that way); a tile wholly
+//     inside its tensor moves its master weights, grads and bf16 copy with
+//     wave accesses over 1 KB of consecutive bytes, re-laid between the two
+//     layouts by a cross-lane swap (grads) and a per-wave LDS area;
 //   * a group of G elements spans G/16 lanes of one wave; group statistics
 //     are DPP butterfly reductions across those lanes, no LDS round trip;
-//   * moments are dequantized, updated and reduced in fp64 (CDNA4 runs fp64
-//     FMA at the fp32 rate): the group's k and s are ill-conditioned in its
-//     smallest |m'|, usually a near-cancellation of b1*m and (1-b1)*g, so the
-//     per-element chain carries 53 bits;
+//   * moments are dequantized, updated and reduced in fp64 (an fp64 FMA
+//     issues in about 1.4 times the time of an fp32 one here): the group's k
+//     and s are ill-conditioned in its smallest |m'|, usually a
+//     near-cancellation of b1*m and (1-b1)*g, so the per-element chain
+//     carries 53 bits;
 //   * the per-group scalar work (k, s, the dequantization constants) runs
 //     once per lane pair: the even lane of a pair does the first moment, the
 //     odd lane the second, and the pair swaps results through DPP;
@@ -821,12 +825,12 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
     return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
 }
 
-// Inputs of one wavefront tile.
 // One tile's inputs in registers. Tiles that end inside their tensor: the
-// lane's own 16 elements throughout. Whole tiles (load_full_tile): codes and
-// the stored state as above, the grads 8 per lane per half tile (elements
-// 512 h + 8 lane + j) and the master weights 4 per lane per quarter tile
-// (elements 256 i + 4 lane + j, p[4 i + j]).
+// lane's own 16 elements of every stream. Whole tiles (load_full_tile): the
+// codes of the lane's own 16 elements and the stored state of its group, the
+// grads 8 per lane per half tile (elements 512 h + 8 lane + j, re-laid before
+// use) and the master weights 4 per lane per quarter tile (elements
+// 256 i + 4 lane + j, p[4 i + j]).
 struct TileIn {
     float p[16];
     uint32_t gw[8], mq[4], vq[4];
