@@ -14,10 +14,14 @@ namespace {
 // s = 0), value = RN_bf16(RN32(decode(code) s)); a tensor or group holding a
 // NaN or Inf gets s = NaN and every code 0x7F.
 //
-// The codes come from x * (1 / s) through the hardware converts; x * (1/s)
-// is within 2 ulp of RN32(x / s), so only a value within kAmbiguity of an
-// FP8 rounding midpoint can round differently, and those are redone from the
-// exact quotient.
+// RN32(x / s) without a division per value: x has at most 8 significant bits
+// and s at most 24, so a quotient that is not an fp32 number lies at least
+// 2^-49 (relative) from every midpoint between fp32 neighbours (the distance
+// is a nonzero multiple of 2^(e-24) / s's integer significand in the binade
+// [2^e, 2^(e+1)), likewise in the subnormal range), while x * RN64(1 / s),
+// rounded to fp64, is within 2^-52 of it. Rounding that product to fp32 thus
+// gives RN32(x / s) exactly; the hardware converts round it to the FP8 grid,
+// nearest with ties to even, after a clamp to the largest finite magnitude.
 
 // bf16 magnitude bits of 16 values (two 16-byte words per 8 values) -> max.
 __device__ __forceinline__ uint32_t bf16_absmax_bits(const uint32_t (&w)[8]) {
@@ -65,38 +69,19 @@ __device__ __forceinline__ void act_codes16(const uint32_t (&w)[8], uint32_t ama
         }
         return;
     }
-    // A subnormal scale (amax below 2^-117 or so) has a reciprocal beyond the
-    // fp32 range: every element of such a group takes the exact path.
-    const uint32_t all = sc < 0x1p-126f ? 0x80808080u : 0u;
-    const float r = 1.0f / sc;
+    const double r = 1.0 / (double)sc;  // RN64(1 / s); fp64 holds it for a subnormal s too
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float x[4], lo[4], hi[4];
+        float y[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int j = 4 * i + b;
-            x[b] = __builtin_bit_cast(float, (j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16));
-            const float a = __builtin_fabsf(x[b]) * r;
-            lo[b] = __builtin_copysignf(__builtin_fminf(a * (1.0f - kAmbiguity), T::FPMAX_F), x[b]);
-            hi[b] = __builtin_fminf(a * (1.0f + kAmbiguity), T::FPMAX_F);
+            const float x = __builtin_bit_cast(float, (j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16));
+            const float q = (float)((double)x * r);  // RN32(x / s)
+            y[b] = __builtin_fminf(__builtin_fmaxf(q, -T::FPMAX_F), T::FPMAX_F);
         }
-        uint32_t wl = cvt_pk<F, false>(lo[0], lo[1], 0u);
-        wl = cvt_pk<F, true>(lo[2], lo[3], wl);
-        uint32_t wh = cvt_pk<F, false>(hi[0], hi[1], 0u);
-        wh = cvt_pk<F, true>(hi[2], hi[3], wh);
-        const uint32_t d = ((((wl ^ wh) & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u) | all;
-        if (d) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                if ((d >> (8 * b + 7)) & 1u) {
-                    const float y = (float)((double)x[b] / (double)sc);  // RN32(x / s)
-                    const uint32_t c = (__builtin_signbit(x[b]) ? 0x80u : 0u) |
-                                       encode_mag_exact<F>(__builtin_fabs((double)y));
-                    wl = (wl & ~(0xFFu << (8 * b))) | (c << (8 * b));
-                }
-            }
-        }
-        out[i] = wl;
+        uint32_t c = cvt_pk<F, false>(y[0], y[1], 0u);
+        out[i] = cvt_pk<F, true>(y[2], y[3], c);
     }
 }
 

@@ -93,6 +93,30 @@ def test_edge_groups(coat, fmt):
 
 
 @pytest.mark.parametrize("fmt", [E4, E5])
+def test_every_bf16_value_per_tensor(coat, fmt):
+    """Every finite bf16 value up to the tensor's maximum, coded with one scale:
+    for a maximum of fpmax * 2^k the scale is 2^k exactly, so the quotients are
+    the bf16 values themselves scaled, every FP8 rounding midpoint of the grid
+    among them (ties), subnormal codes included; other maxima give scales
+    with full 24-bit significands. Codes, scale and bf16 values equal the
+    oracle's bit for bit."""
+    fpmax = 448.0 if fmt == E4 else 57344.0
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    fin = (allb & 0x7F80) != 0x7F80
+    f32 = (allb.astype(np.uint32) << 16).view(np.float32)
+    rng = np.random.default_rng(11 + fmt)
+    amaxes = [fpmax * 2.0 ** k for k in (-120, -40, -8, 0, 9, 60, 110)]
+    amaxes += [float(np.float32(v)) for v in rng.uniform(1e-3, 1e3, 4)]
+    for amax in amaxes:
+        am = torch.tensor([amax], dtype=torch.float32).to(torch.bfloat16)
+        amf = float(am.float())
+        keep = fin & (np.abs(f32) <= amf)
+        xs = np.concatenate([allb[keep], bits(am), bits(-am)])
+        xb = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16)
+        check(coat, xb, 0, fmt, f"all-bf16 amax={amf:.4g}")
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
 def test_decode_every_code(coat, fmt):
     q = torch.arange(256, dtype=torch.uint8, device="cuda").repeat(4)
     s = torch.ones(1, dtype=torch.float32, device="cuda")
