@@ -130,9 +130,10 @@ typedef struct coat_multi_plan {
  * Validate `count` descriptors (host array) and enqueue on `stream` their copy,
  * with a tile table, into `workspace` (device memory, 256-byte aligned, at
  * least coat_multi_workspace_bytes(count) bytes). The tables travel in the
- * arguments of a few small copy launches (about 3 KB each), so the call
- * neither stages through host memory nor waits: it returns once they are
- * enqueued, and the host array `tensors` is read during the call only. Steps
+ * arguments of small copy launches, one per 3 KB of tables (11 for the 363
+ * tensors of a Llama-2-13B list), so the call neither stages through host
+ * memory nor waits: it returns once they are enqueued, and the host array
+ * `tensors` is read during the call only. Steps
  * enqueued after it on the same stream see the tables; a step on another
  * stream must be ordered after them by the caller. The plan stays valid while
  * the tensors' buffers and the workspace do. COAT_EHIP (a refused launch) may
