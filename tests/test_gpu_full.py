@@ -155,3 +155,76 @@ def test_full_size_sampled(coat, name):
 def test_full_size_dense(coat, name):
     met = run_full(coat, name, every=int(os.environ["COAT_DENSE_PARITY"]))
     assert met["m_k_rel"] < 1e-6 and met["v_k_rel"] < 1e-6
+
+
+def test_tensor_beyond_2_32_elements(coat):
+    """One tensor of 2^32 + 5632 elements (a partial last tile) between two small
+    ones: element, group and tile indices past 2^31 and 2^32 in the planned
+    multi-tensor launch and in the single-tensor entry point. Sampled groups
+    (around elements 2^31 and 2^32, the first and last groups, the partial
+    tile, and a stride through the tensor) against the oracle; the
+    single-tensor call equals the planned launch bit for bit there."""
+    G, fm, fv = 128, 0, 1
+    big = (1 << 32) + 5 * 1024 + 512
+    sizes = [3200, big, 896]
+    wl = synth.Workload("beyond-2^32", tuple((f"t{i}", (n,)) for i, n in enumerate(sizes)), G, fm, fv, seed=29)
+    dev = torch.device("cuda")
+    ngb = big // G
+    picks = set([0, 1, ngb - 1, ngb - 2, ngb - 3, ngb - 4, ngb - 5])
+    for c in ((1 << 31) // G, (1 << 32) // G):
+        picks.update(range(c - 3, c + 3))
+    picks.update(range(7, ngb, 99991))
+    sample = [(0, list(range(sizes[0] // G))), (1, sorted(picks)), (2, list(range(sizes[2] // G)))]
+    chunk = 1 << 28  # prior moments generated in chunks of whole groups (fp64 temporaries)
+
+    def make():
+        st = coat.ParamListState(sizes, G, device=dev)
+        host = []
+        for i, n in enumerate(sizes):
+            t = st.tensor(i)
+            synth.params(n, wl.seed, i, device=dev, out=t.params)
+            synth.grads(n, wl.seed, i, device=dev, out=t.grads)
+            idx = torch.tensor(sample[i][1], dtype=torch.long, device=dev)
+            ms_, vs_ = [], []
+            for c0 in range(0, n, chunk):
+                cn = min(chunk, n - c0)
+                m, v = synth.prior_moments(cn, G, wl.seed, 1000 * i + c0 // chunk, device=dev)
+                g0, g1 = c0 // G, (c0 + cn) // G
+                coat.quantize(m, t.m_q[c0:c0 + cn], t.m_s[g0:g1], t.m_k[g0:g1], group=G, fmt=fm)
+                coat.quantize(v, t.v_q[c0:c0 + cn], t.v_s[g0:g1], t.v_k[g0:g1], group=G, fmt=fv)
+                sel = idx[(idx >= g0) & (idx < g1)] - g0
+                ms_.append(gather(m, G, sel))
+                vs_.append(gather(v, G, sel))
+                del m, v
+            host.append(dict(idx=idx, p=gather(t.params, G, idx),
+                             g=bf16_bits(t.grads.view(-1, G)[idx].reshape(-1).cpu()),
+                             m=np.concatenate(ms_), v=np.concatenate(vs_)))
+        torch.cuda.synchronize()
+        oracle_quantize_sample(host, wl)
+        overwrite_sample(st, host, G)
+        return st, host
+
+    h = HYPER
+    kw = dict(fmt_m=fm, fmt_v=fv, lr=h["lr"], beta1=h["b1"], beta2=h["b2"], eps=h["eps"],
+              weight_decay=h["wd"], step=h["step"])
+    log(f"test_tensor_beyond_2_32_elements sizes={sizes}")
+    st, host = make()
+    log("  inputs on device")
+    st.step(**kw)
+    torch.cuda.synchronize()
+    got = read_sample(st, host, G)
+    del st
+    torch.cuda.empty_cache()
+    compare(concat(got), concat(oracle_steps(host, wl, h["step"])), "beyond-2^32 planned")
+    st2, host2 = make()
+    for i in range(len(sizes)):
+        t = st2.tensor(i)
+        coat.adamw_step(t.params, t.params_bf16, t.grads, t.m_q, t.m_s, t.m_k, t.v_q, t.v_s, t.v_k, group=G, **kw)
+    torch.cuda.synchronize()
+    got2 = read_sample(st2, host2, G)
+    del st2
+    torch.cuda.empty_cache()
+    for a, b in zip(got, got2):
+        for key in a:
+            assert np.array_equal(a[key], b[key], equal_nan=True), key
+    log("  single-tensor calls equal the planned launch on the sample")
