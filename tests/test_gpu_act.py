@@ -169,3 +169,52 @@ def test_full_size_llama13b_mlp(coat, G):
     assert int(np.sum(q[it].cpu().numpy() != oq)) == 0
     assert same_bf16(bits(back[it]), oracle.act_dequantize(oq, os_, G, fmt))
     log(f"[act full per-group] n={n} sampled groups {groups.size}")
+
+
+@pytest.mark.parametrize("G", [0, 128])
+def test_act_beyond_2_32_elements(coat, G):
+    """Activation codec on 2^32 + 2148 bf16 values (a short last group): groups
+    around elements 2^31 and 2^32, the first and last groups and a stride
+    through the buffer, codes, scales and bf16 values against the oracle. Per
+    tensor, the largest magnitude sits past 2^32 and the sample holds it, so
+    the oracle's scale over the sample is the tensor's."""
+    fmt = E4
+    n = (1 << 32) + 2 * 1024 + 100
+    chunk = 1 << 28
+    x = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    gen = torch.Generator(device="cuda")
+    for c0 in range(0, n, chunk):
+        cn = min(chunk, n - c0)
+        gen.manual_seed(7001 + c0 // chunk)
+        x[c0:c0 + cn] = torch.randn(cn, device="cuda", generator=gen).mul_(0.5)
+    top = (1 << 32) + 5
+    x[top] = -1e4  # larger in magnitude than any other value
+    q = torch.empty(n, dtype=torch.uint8, device="cuda")
+    s = torch.empty(coat.act_nscales(n, G), dtype=torch.float32, device="cuda")
+    log(f"test_act_beyond_2_32_elements G={G} n={n}")
+    coat.act_quantize(x, q, s, group=G, fmt=fmt)
+    back = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    coat.act_dequantize(q, s, back, group=G, fmt=fmt)
+    torch.cuda.synchronize()
+    Gs = G or 128  # sampling unit
+    nu = (n + Gs - 1) // Gs
+    picks = set([0, 1, nu - 1, nu - 2, top // Gs])
+    for c in ((1 << 31) // Gs, (1 << 32) // Gs):
+        picks.update(range(c - 3, c + 3))
+    picks.update(range(9, nu, 99991))
+    spans = [(u * Gs, min(n, u * Gs + Gs)) for u in sorted(picks)]
+    xs = np.concatenate([bits(x[a:b]) for a, b in spans])
+    qs = np.concatenate([q[a:b].cpu().numpy() for a, b in spans])
+    bs = np.concatenate([bits(back[a:b]) for a, b in spans])
+    if G:
+        # each sampled group on its own (the last one short)
+        for (a, b), off in zip(spans, np.cumsum([0] + [b - a for a, b in spans[:-1]])):
+            oq, os_ = oracle.act_quantize(xs[off:off + b - a], G, fmt)
+            assert np.array_equal(qs[off:off + b - a], oq)
+            assert same_f32(s[a // G:a // G + 1].cpu().numpy(), os_)
+            assert same_bf16(bs[off:off + b - a], oracle.act_dequantize(oq, os_, G, fmt))
+    else:
+        oq, os_ = oracle.act_quantize(xs, 0, fmt)
+        assert same_f32(s.cpu().numpy(), os_)
+        assert np.array_equal(qs, oq)
+        assert same_bf16(bs, oracle.act_dequantize(oq, os_, 0, fmt))

@@ -215,3 +215,49 @@ def test_quantize_near_constant_threshold(coat, G):
     assert rel_err(S.cpu().numpy(), s).max() <= 1e-5
     d = code_steps(Q.cpu().numpy(), q)
     assert d.max() <= 1 and (d != 0).mean() <= 1e-4
+
+
+def test_codec_beyond_2_32_elements(coat):
+    """Quantize and dequantize one buffer of 2^32 + 3149 moment values (a short
+    last group): groups around elements 2^31 and 2^32, the first and the last
+    groups and a stride through the buffer, against the oracle."""
+    import synth
+    G, fmt = 128, E4
+    n = (1 << 32) + 3 * 1024 + 77
+    ng = (n + G - 1) // G
+    chunk = 1 << 28  # whole groups; fp64 temporaries per chunk
+    X = torch.empty(n, dtype=torch.float32, device="cuda")
+    for c0 in range(0, n, chunk):
+        cn = min(chunk, n - c0)
+        m, _ = synth.prior_moments(cn, G, 31, c0 // chunk, device="cuda")
+        X[c0:c0 + cn] = m
+        del m
+    Q = torch.empty(n, dtype=torch.uint8, device="cuda")
+    S = torch.empty(ng, dtype=torch.float64, device="cuda")
+    K = torch.empty(ng, dtype=torch.float32, device="cuda")
+    log(f"test_codec_beyond_2_32_elements n={n}")
+    coat.quantize(X, Q, S, K, group=G, fmt=fmt)
+    back = torch.empty(n, dtype=torch.float32, device="cuda")
+    coat.dequantize(Q, S, K, back, group=G, fmt=fmt)
+    torch.cuda.synchronize()
+    picks = set([0, 1, ng - 1, ng - 2])
+    for c in ((1 << 31) // G, (1 << 32) // G):
+        picks.update(range(c - 3, c + 3))
+    picks.update(range(5, ng, 99991))
+    kd, sd, steps, deq = [], [], [], []
+    for gi in sorted(picks):
+        a, b = gi * G, min(n, gi * G + G)
+        x = X[a:b].cpu().numpy().astype(np.float64)
+        q, s, k = oracle.quantize(x, G, fmt)
+        kd.append(rel_err(K[gi:gi + 1].cpu().numpy(), k).max())
+        sd.append(rel_err(S[gi:gi + 1].cpu().numpy(), s).max())
+        qg = Q[a:b].cpu().numpy()
+        steps.append(code_steps(qg, q))
+        want = oracle.dequantize(qg, S[gi:gi + 1].cpu().numpy(), K[gi:gi + 1].cpu().numpy(), G, fmt)
+        got = back[a:b].cpu().numpy().astype(np.float64)
+        deq.append(np.all(np.abs(got - want) <= np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)))
+    d = np.concatenate(steps)
+    log(f"  {len(picks)} groups: k rel max {max(kd):.3g}, s rel max {max(sd):.3g}, codes differing {int((d != 0).sum())}")
+    assert max(kd) <= 1e-5 and max(sd) <= 1e-5
+    assert d.max() <= 1 and (d != 0).mean() <= 1e-4
+    assert all(deq)
