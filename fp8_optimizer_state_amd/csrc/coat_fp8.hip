@@ -595,6 +595,11 @@ __device__ NewGroup new_group(double amax, double amin, double L, double L_lo, d
     g.k = k;
     g.r = rcp_f64((double)k);
     g.s = exp2_full((double)k * L - F.log2_fpmax);
+    // k = 1: s is the plain quotient amax / fpmax, as defined (rare with
+    // expansion: near-constant groups)
+    if (__builtin_expect(__any(k == 1.0f), 0)) {
+        if (k == 1.0f) g.s = amax / F.fpmax;
+    }
     g.ia = (float)rcp_f64_1(amax);
     g.w = __builtin_fmaf(kAmbW1, k, F.amb_w0);
     // The fp32 path needs every member and 1/amax normal in fp32 and |x| / amax
@@ -712,6 +717,44 @@ __device__ __forceinline__ double dequant_mag(uint32_t w, int i, const OldGroup&
 }
 
 
+// Groups stored with k = 1 (near-constant or all-zero groups, and every group
+// without expansion): the dequantized magnitude is the plain product |q| s
+// and the new moment b x + c g takes the definition's two roundings,
+// RN(RN(b x) + RN(c g)), so that such groups carry the defining arithmetic
+// exactly from step to step. Such a group's OldGroup has r = 1 exactly
+// (k1_mark); where the rare paths read it back, its a_lo holds s instead of
+// the low part of a (k1_group: the exact k = 1 formula needs s, the general
+// one is not used for it there). The code's value comes from the hardware OCP
+// convert, exact in fp32 (a NaN code gives NaN, the E5M2 Inf code Inf; times
+// s: Inf, or NaN for s = 0).
+template <int F>
+__device__ __forceinline__ double code_value(uint32_t w, int i) {
+    const int b = (int)(w >> (8 * i));
+    if constexpr (F == COAT_FMT_E4M3)
+        return (double)__builtin_amdgcn_cvt_f32_fp8(b, 0);
+    else
+        return (double)__builtin_amdgcn_cvt_f32_bf8(b, 0);
+}
+// Byte i of code word w: RN(RN(b x) + cg), x = sign(q) RN(|q| s).
+template <int F>
+__device__ __forceinline__ double k1_moment(uint32_t w, int i, double s, double b, double cg) {
+    const double x = code_value<F>(w, i) * s;
+    const double bx = b * x;
+    return bx + cg;
+}
+__device__ __forceinline__ OldGroup k1_mark(OldGroup g, float k) {
+    if (k == 1.0f) g.r = 1.0;
+    return g;
+}
+__device__ __forceinline__ OldGroup k1_group(OldGroup g, double s, float k) {
+    if (k == 1.0f) {
+        g.r = 1.0;
+        g.a_lo = s;
+    }
+    return g;
+}
+__device__ __forceinline__ bool is_k1(const OldGroup& g) { return g.r == 1.0; }
+
 __device__ __forceinline__ uint32_t select4(int i, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
     return i == 0 ? a0 : (i == 1 ? a1 : (i == 2 ? a2 : a3));
 }
@@ -784,7 +827,7 @@ struct ParkTab {
 template <int F, typename OW, typename GW, typename L>
 __device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&codes)[4], OW old_word, GW grad_word,
                                                const OldGroup& og, const NewGroup& ng, const L& lq, const double* lqm,
-                                               const FmtRT& F_, double cb, bool square, CoefPtr cf) {
+                                               const FmtRT& F_, double b, double cb, bool square, CoefPtr cf) {
     while (__any((amb[0] | amb[1] | amb[2] | amb[3]) != 0u)) {
         if ((amb[0] | amb[1] | amb[2] | amb[3]) != 0u) {
             const int wi = amb[0] ? 0 : (amb[1] ? 1 : (amb[2] ? 2 : 3));
@@ -795,7 +838,8 @@ __device__ __forceinline__ void redo_ambiguous(uint32_t (&amb)[4], uint32_t (&co
             const double g = bf16_to_f64(grad_word(e >> 1), e & 1);
             double tb;
             const double mag = dequant_mag(oldw >> (8 * bi), 0, og, lq, tb);
-            const double x = __builtin_fma(tb, mag, cb * (square ? g * g : g));
+            const double cgx = square ? (cb * g) * g : cb * g;
+            const double x = is_k1(og) ? k1_moment<F>(oldw, bi, og.a_lo, b, cgx) : __builtin_fma(tb, mag, cgx);
             const uint32_t fastw = select4(wi, codes[0], codes[1], codes[2], codes[3]);
             const uint32_t lo = byte_of(fastw, bi) & 0x7Fu;
             uint32_t code;
@@ -1049,6 +1093,43 @@ __device__ __forceinline__ void build_tables(WaveLdsTab& wl, const TabTables& ct
     asm volatile("" ::: "memory");
 }
 
+// The tables of a moment stored with k = 1, rebuilt by the same builder lanes
+// after build_tables: TE[e] = 2^(max(e,1) - BIAS - MB) exactly and
+// TS[+-i] = +-RN(b RN(i s)), so that a code's TE TS, an exact product, is
+// RN(b RN(|q| s)) and the element pass's fma(TE, TS, c g) forms
+// RN(RN(b x) + RN(c g)), the definition's two roundings (see k1_moment).
+// The special entries (NaN, Inf) stay as built.
+template <int FM, int FV>
+__device__ __forceinline__ void k1_tables(WaveLdsTab& wl, int lpg, double s, float k, double b1, double b2) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int l = lane & (lpg - 1);
+    if (l >= 8 || k != 1.0f) return;
+    const int mu = l >> 2, t = l & 3;
+    const bool e4 = (mu ? FV : FM) == COAT_FMT_E4M3;
+    const int bias = e4 ? Fmt<COAT_FMT_E4M3>::BIAS : Fmt<COAT_FMT_E5M2>::BIAS;
+    const int mb = e4 ? Fmt<COAT_FMT_E4M3>::MB : Fmt<COAT_FMT_E5M2>::MB;
+    const int nte = e4 ? 16 : 31;       // TE entries below the special one
+    const int nts = 2 << mb;            // significands 0 .. 2^(MB+1) - 1; NEG = nts
+    const int tsb = e4 ? ts_base<COAT_FMT_E4M3>() : ts_base<COAT_FMT_E5M2>();
+    const double b = mu ? b2 : b1;
+    double* g = reinterpret_cast<double*>(&wl.tbl[(lane / lpg) * 2 + mu]);
+    for (int e = t; e < nte; e += 4) g[e] = __builtin_amdgcn_ldexp(1.0, (e > 0 ? e : 1) - bias - mb);
+    for (int i = t; i < nts; i += 4) {
+        const double v = b * ((double)i * s);
+        g[tsb + i] = v;
+        g[tsb + i + nts] = -v;
+    }
+    asm volatile("" ::: "memory");
+}
+
+// The same out of line, for kernels in which k = 1 groups are rare (a call
+// keeps its registers off the tile loop).
+template <int FM, int FV>
+__device__ __attribute__((noinline)) void k1_tables_cold(WaveLdsTab& wl, int lpg, double s, float k, double b1,
+                                                         double b2) {
+    k1_tables<FM, FV>(wl, lpg, s, k, b1, b2);
+}
+
 // The group-table offsets (TE, TS) of byte i of code word w, packed low / high.
 __device__ __forceinline__ uint32_t code_offsets(uint32_t w, int i, const uint32_t* lut) {
     return lut[(w >> (8 * i)) & 0xFFu];
@@ -1082,8 +1163,9 @@ __device__ __forceinline__ void parked_old_groups(const PK& pk, OldGroup& gm, Ol
     if constexpr (TAB) {
         const FmtRT fm = fmt_rt<FM>(), fv = fmt_rt<FV>();
         const bool q_odd = ((lane >> 2) & 1) != 0;
-        const OldGroup mine = old_group(pk.s[lane], pk.k[lane], q_odd ? fv.log2_fpmax : fm.log2_fpmax,
-                                        q_odd ? fv.log2_fpmax_lo : fm.log2_fpmax_lo);
+        const OldGroup mine = k1_group(old_group(pk.s[lane], pk.k[lane], q_odd ? fv.log2_fpmax : fm.log2_fpmax,
+                                                 q_odd ? fv.log2_fpmax_lo : fm.log2_fpmax_lo),
+                                       pk.s[lane], pk.k[lane]);
         const OldGroup other{xlane64(mine.a, 4), xlane64(mine.a_lo, 4), xlane64(mine.r, 4), xlane64(mine.r_lo, 4)};
         gm = q_odd ? other : mine;
         gv = q_odd ? mine : other;
@@ -1107,7 +1189,7 @@ struct RareStats {
     uint32_t redone;    // the lane's elements whose update was redone in fp64
     uint32_t any_wide;  // some lane of the wave redid one
 };
-template <typename LQ, typename CW, typename GW, typename P0, typename OW>
+template <int FM, int FV, typename LQ, typename CW, typename GW, typename P0, typename OW>
 __device__ __forceinline__ RareStats rare_stats(const OldGroup& pm, const OldGroup& pv, const LQ& lq_m,
                                                 const LQ& lq_v, const StepConsts& c, int nvalid, CW code_word,
                                                 GW grad_word, P0 p0, OW on_wide) {
@@ -1122,8 +1204,10 @@ __device__ __forceinline__ RareStats rare_stats(const OldGroup& pm, const OldGro
         double tbm, tbv;
         const double m0 = dequant_mag(wm >> (8 * (i & 3)), 0, pm, lq_m, tbm);
         const double v0 = dequant_mag(wv >> (8 * (i & 3)), 0, pv, lq_v, tbv);
-        const double m1 = __builtin_fma(tbm, m0, c.c1 * g);
-        const double v1 = __builtin_fma(tbv, v0, c.c2 * (g * g));
+        const double m1 = is_k1(pm) ? k1_moment<FM>(wm, i & 3, pm.a_lo, c.b1, c.c1 * g)
+                                    : __builtin_fma(tbm, m0, c.c1 * g);
+        const double v1 = is_k1(pv) ? k1_moment<FV>(wv, i & 3, pv.a_lo, c.b2, (c.c2 * g) * g)
+                                    : __builtin_fma(tbv, v0, (c.c2 * g) * g);
         const double am = __builtin_fabs(m1), av = __builtin_fabs(v1);
         const bool fin_m = am < __builtin_inf(), fin_v = av < __builtin_inf();
         r.bad |= (fin_m ? 0u : 1u) | (fin_v ? 0u : 2u);
@@ -1143,10 +1227,13 @@ __device__ __forceinline__ RareStats rare_stats(const OldGroup& pm, const OldGro
             r.redone |= 1u << i;
             const double g = bf16_to_f64(grad_word(i >> 1), i & 1);
             double tbm, tbv;
-            const double m0 = dequant_mag(code_word(false, i >> 2) >> (8 * (i & 3)), 0, pm, lq_m, tbm);
-            const double v0 = dequant_mag(code_word(true, i >> 2) >> (8 * (i & 3)), 0, pv, lq_v, tbv);
-            const double m1 = __builtin_fma(tbm, m0, c.c1 * g);
-            const double v1 = __builtin_fma(tbv, v0, c.c2 * (g * g));
+            const uint32_t wm = code_word(false, i >> 2), wv = code_word(true, i >> 2);
+            const double m0 = dequant_mag(wm >> (8 * (i & 3)), 0, pm, lq_m, tbm);
+            const double v0 = dequant_mag(wv >> (8 * (i & 3)), 0, pv, lq_v, tbv);
+            const double m1 = is_k1(pm) ? k1_moment<FM>(wm, i & 3, pm.a_lo, c.b1, c.c1 * g)
+                                        : __builtin_fma(tbm, m0, c.c1 * g);
+            const double v1 = is_k1(pv) ? k1_moment<FV>(wv, i & 3, pv.a_lo, c.b2, (c.c2 * g) * g)
+                                        : __builtin_fma(tbv, v0, (c.c2 * g) * g);
             const double den = __builtin_sqrt(v1) * (double)c.ib2 + (double)c.eps;
             on_wide(i, (float)((double)p0(i) * (double)c.decay - (double)c.ssz * (m1 / den)));
         }
@@ -1154,7 +1241,7 @@ __device__ __forceinline__ RareStats rare_stats(const OldGroup& pm, const OldGro
     return r;
 }
 
-template <int FM, int FV, bool FULL, bool TAB, int LG>
+template <int FM, int FV, bool FULL, bool TAB, int LG, bool K1 = false>
 __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, const StepConsts& c,
                                           const typename StepLds<TAB>::Tables& ct,
                                           typename StepLds<TAB>::Wave& wl, TileIn& in) {
@@ -1194,14 +1281,15 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     // active: the pair split exchanges results between lanes)
     auto groups_of = [&](double s0, float k0, double s1, float k1, OldGroup& gm, OldGroup& gv) {
         if (pair) {
-            const OldGroup mine = old_group(s0, k0, odd ? fv.log2_fpmax : fm.log2_fpmax,
-                                            odd ? fv.log2_fpmax_lo : fm.log2_fpmax_lo);
+            const OldGroup mine = k1_mark(old_group(s0, k0, odd ? fv.log2_fpmax : fm.log2_fpmax,
+                                                    odd ? fv.log2_fpmax_lo : fm.log2_fpmax_lo),
+                                          k0);
             const OldGroup other = swap_pair(mine);
             gm = odd ? other : mine;
             gv = odd ? mine : other;
         } else {
-            gm = old_group(s0, k0, fm.log2_fpmax, fm.log2_fpmax_lo);
-            gv = old_group(s1, k1, fv.log2_fpmax, fv.log2_fpmax_lo);
+            gm = k1_mark(old_group(s0, k0, fm.log2_fpmax, fm.log2_fpmax_lo), k0);
+            gv = k1_mark(old_group(s1, k1, fv.log2_fpmax, fv.log2_fpmax_lo), k1);
         }
     };
     // Table path: a lane holds the state of moment (lane >> 2) & 1, the one
@@ -1213,7 +1301,27 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     // the same from the parked state (rare paths, after the element pass)
     auto parked_groups = [&](OldGroup& gm, OldGroup& gv) { parked_old_groups<FM, FV, TAB>(pk, gm, gv); };
     OldGroup om, ov;
-    if constexpr (!TAB) groups_of(in.s0, in.k0, in.s1, in.k1, om, ov);
+    // Direct path: the dequantization constants are parked at once (the rare
+    // paths read them back after the element pass); a group stored with k = 1
+    // parks its s in place of a_lo (k1_group), from where the exact k = 1
+    // element pass also reads it.
+    bool k1_wave = false;  // some group of the wave stored with k = 1
+    if constexpr (!TAB) {
+        groups_of(in.s0, in.k0, in.s1, in.k1, om, ov);
+        pk.og[0][lane] = om.a; pk.og[1][lane] = om.a_lo; pk.og[2][lane] = om.r;
+        pk.og[3][lane] = ov.a; pk.og[4][lane] = ov.a_lo; pk.og[5][lane] = ov.r;
+        k1_wave = __any(is_k1(om) || is_k1(ov));
+        if (__builtin_expect(k1_wave, 0)) {
+            double sm = in.s0, sv = in.s1;
+            if (pair) {
+                const double other = dpp64<kDppXor1>(in.s0);
+                sm = odd ? other : in.s0;
+                sv = odd ? in.s0 : other;
+            }
+            if (is_k1(om)) pk.og[1][lane] = sm;
+            if (is_k1(ov)) pk.og[4][lane] = sv;
+        }
+    }
     // Whole tiles: the grads as loaded hold chunks 2 l and 2 l + 1 of the
     // lane's half of the tile (l = lane mod 32) split between lanes l and
     // l + 32 (lane l: its own even chunk and, in the second half's words, lane
@@ -1236,6 +1344,7 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     const auto lq_v = lq_source(ct, 1, c.b2);
     float xm[16], xv[16];
     double amax_m = 0.0, amin_m = __builtin_inf(), amax_v = 0.0, amin_v = __builtin_inf();
+    bool k1_mixed = false;  // wave-uniform: see the direct element pass
     // sum of xm * xv: not finite if any moment is infinite or NaN (or beyond fp32)
     float fin = 0.0f;
     // upd(i, cg, cg2, m1, v1): the new moments of element i from c1 g and c2 g^2
@@ -1244,7 +1353,7 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
         for (int i = 0; i < 16; ++i) {
             const double g = bf16_to_f64(gw[i >> 1], i & 1);
             double m1, v1;
-            upd_moments(i, c.c1 * g, c.c2 * (g * g), m1, v1);
+            upd_moments(i, c.c1 * g, (c.c2 * g) * g, m1, v1);
             amax_m = vmax_abs(amax_m, m1);
             amin_m = vmin_abs(amin_m, m1);
             amax_v = vmax_abs(amax_v, v1);
@@ -1282,7 +1391,18 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     };
     if constexpr (TAB) {
         // groups of 128 and more: per-group tables
-        build_tables<FM, FV>(wl, ct, own_group(in.s0, in.k0), lpg);
+        // K1 (launches without expansion, where every group is stored with
+        // k = 1 after the first step): a wave whose groups all have k = 1
+        // builds only the exact k = 1 tables
+        if (K1 && __all(in.k0 == 1.0f)) {
+            k1_tables<FM, FV>(wl, lpg, in.s0, in.k0, c.b1, c.b2);
+        } else {
+            build_tables<FM, FV>(wl, ct, own_group(in.s0, in.k0), lpg);
+            if (__builtin_expect(__any(in.k0 == 1.0f), 0)) {
+                if constexpr (K1) k1_tables<FM, FV>(wl, lpg, in.s0, in.k0, c.b1, c.b2);
+                else k1_tables_cold<FM, FV>(wl, lpg, in.s0, in.k0, c.b1, c.b2);
+            }
+        }
         const GroupTable& tm = wl.tbl[(lane / lpg) * 2];
         const GroupTable& tv = wl.tbl[(lane / lpg) * 2 + 1];
         // Software-pipelined: element i's group-table reads are issued before
@@ -1304,17 +1424,30 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
         asm volatile("" ::: "memory");  // the park area reuses the tables' LDS
     } else {
         own_grads();
-        element_pass([&](int i, double cg, double cg2, double& m1, double& v1) {
-            double tbm, tbv;
-            const double m0 = dequant_mag(mq[i >> 2], i & 3, om, lq_m, tbm);
-            const double v0 = dequant_mag(vq[i >> 2], i & 3, ov, lq_v, tbv);
-            m1 = __builtin_fma(tbm, m0, cg);
-            v1 = __builtin_fma(tbv, v0, cg2);
-        });
+        if (!K1 || __builtin_expect(!k1_wave, 1) || !__all(is_k1(om) && is_k1(ov))) {
+            // (a wave with k = 1 groups takes this pass, then the exact
+            // statistics path below, which treats the k = 1 groups exactly;
+            // K1 kernels have a pass of their own for waves of k = 1 groups)
+            element_pass([&](int i, double cg, double cg2, double& m1, double& v1) {
+                double tbm, tbv;
+                const double m0 = dequant_mag(mq[i >> 2], i & 3, om, lq_m, tbm);
+                const double v0 = dequant_mag(vq[i >> 2], i & 3, ov, lq_v, tbv);
+                m1 = __builtin_fma(tbm, m0, cg);
+                v1 = __builtin_fma(tbv, v0, cg2);
+            });
+            k1_mixed = k1_wave;
+        } else {
+            // every group of the wave stored with k = 1 (e.g. no expansion)
+            const double sm = pk.og[1][lane], sv = pk.og[4][lane];
+            element_pass([&](int i, double cg, double cg2, double& m1, double& v1) {
+                m1 = k1_moment<FM>(mq[i >> 2], i & 3, sm, c.b1, cg);
+                v1 = k1_moment<FV>(vq[i >> 2], i & 3, sv, c.b2, cg2);
+            });
+        }
     }
     // A zero moment (the minimum is over nonzero members) or a non-finite one:
     // the statistics are redone exactly.
-    const bool special = amin_m == 0.0 || amin_v == 0.0 || !(__builtin_fabsf(fin) <= 0x1.fffffep+127f);
+    const bool special = amin_m == 0.0 || amin_v == 0.0 || !(__builtin_fabsf(fin) <= 0x1.fffffep+127f) || k1_mixed;
     // ---- park what only the exact paths (statistics with zeros, requantization) need
     if constexpr (!FULL) {
 #pragma unroll
@@ -1325,9 +1458,6 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
     if constexpr (TAB) {
         pk.s[lane] = in.s0;
         pk.k[lane] = in.k0;
-    } else {
-        pk.og[0][lane] = om.a; pk.og[1][lane] = om.a_lo; pk.og[2][lane] = om.r;
-        pk.og[3][lane] = ov.a; pk.og[4][lane] = ov.a_lo; pk.og[5][lane] = ov.r;
     }
     // later reads of the park area must come from LDS, not from registers
     asm volatile("" ::: "memory");
@@ -1361,14 +1491,14 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
         OldGroup pm, pv;
         parked_groups(pm, pv);
         if constexpr (FULL) {
-            r = rare_stats(pm, pv, lq_m, lq_v, c, nvalid, code_word, grad_word,
+            r = rare_stats<FM, FV>(pm, pv, lq_m, lq_v, c, nvalid, code_word, grad_word,
                            [&](int i) { return (P + tile * kTile)[(uint32_t)(16 * lane + i)]; },
                            [&](int i, float pc) {
                                *reinterpret_cast<float*>(X + xfer_off(4 * lane_opaque() + (i >> 2)) + 4 * (i & 3)) = pc;
                            });
             if (r.any_wide) pk.wide[lane] = (uint16_t)r.redone;
         } else {
-            r = rare_stats(pm, pv, lq_m, lq_v, c, nvalid, code_word, grad_word,
+            r = rare_stats<FM, FV>(pm, pv, lq_m, lq_v, c, nvalid, code_word, grad_word,
                            [&](int i) { return P[e0 + i]; },
                            [&](int i, float pc) {
 #pragma unroll
@@ -1543,9 +1673,9 @@ __device__ __forceinline__ void step_tile(const TensorRef& t, int64_t tile, cons
         OldGroup pm, pv;
         parked_groups(pm, pv);
         redo_ambiguous<FM>(am, cm, [&](int w) { return code_word(false, w); }, grad_word, pm, nm, lq_m, ct.lqm[0],
-                           fm, c.c1, false, cf);
+                           fm, c.b1, c.c1, false, cf);
         redo_ambiguous<FV>(av, cv, [&](int w) { return code_word(true, w); }, grad_word, pv, nv, lq_v, ct.lqm[1],
-                           fv, c.c2, true, cf);
+                           fv, c.b2, c.c2, true, cf);
     }
     if (any_flagged) {
         if (nm.flags & kPoison) { cm[0] = cm[1] = cm[2] = cm[3] = 0x7F7F7F7Fu; }
@@ -1574,7 +1704,7 @@ constexpr int kPhasePartial = 2;  // last tiles that end inside their tensor
 // A step over one tensor. TAB (groups of 128 and more): the whole tiles with
 // per-group tables, and nothing else; otherwise the tiles of `phases` on the
 // direct path (group 16: every tile on the general path).
-template <int FM, int FV, bool TAB>
+template <int FM, int FV, bool TAB, bool K1>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAB ? 4 : 3, TAB ? 4 : 3))) void step_single_kernel(
     TensorRef t, StepConsts c, int phases) {
     __shared__ typename StepLds<TAB>::Tables ct;
@@ -1591,7 +1721,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAB ? 4 
             for (int64_t tile = wave_id(); tile < full; tile += nw) {
                 TileIn in;
                 load_full_tile<TAB>(t, tile, c.lg2_group, in);
-                step_tile<FM, FV, true, TAB, 0>(t, tile, c, ct, wl, in);
+                step_tile<FM, FV, true, TAB, 0, K1>(t, tile, c, ct, wl, in);
             }
         }
         first = full;
@@ -1604,7 +1734,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TAB ? 4 
         for (int64_t tile = first + wave_id(); tile < last; tile += nw) {
             TileIn in;
             load_tile(t, tile, c.lg2_group, in);
-            step_tile<FM, FV, false, false, 0>(t, tile, c, ct, wl, in);
+            step_tile<FM, FV, false, false, 0, K1>(t, tile, c, ct, wl, in);
         }
     }
 }
@@ -1651,7 +1781,7 @@ __device__ __forceinline__ void block_full_tiles(const TensorRef* __restrict__ t
 // direct variants run at four waves per SIMD (the direct one spills a few
 // registers outside its tile loop, and its LDS still fits four blocks per
 // CU): on the 13B list at G = 32 that is about 1 % faster than three waves.
-template <int FM, int FV, bool TAB, int LG>
+template <int FM, int FV, bool TAB, int LG, bool K1>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void step_multi_kernel(
     const TensorRef* __restrict__ ts, const int64_t* __restrict__ full_begin, const int32_t* __restrict__ partial,
     int count, int n_partial, StepConsts c, int phases) {
@@ -1668,13 +1798,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
             block_full_tiles(ts, full_begin, count, full, [&](const TensorRef& t, int64_t tile) {
                 TileIn in;
                 load_full_tile<TAB>(t, tile, lg, in);
-                step_tile<FM, FV, true, TAB, LG>(t, tile, c, ct, wl, in);
+                step_tile<FM, FV, true, TAB, LG, K1>(t, tile, c, ct, wl, in);
             });
         } else if constexpr (!TAB) {
             block_full_tiles(ts, full_begin, count, full, [&](const TensorRef& t, int64_t tile) {
                 TileIn in;
                 load_tile(t, tile, lg, in);
-                step_tile<FM, FV, false, false, LG>(t, tile, c, ct, wl, in);
+                step_tile<FM, FV, false, false, LG, K1>(t, tile, c, ct, wl, in);
             });
         }
     }
@@ -1685,7 +1815,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
                 const int64_t tile = t.n / kTile;
                 TileIn in;
                 load_tile(t, tile, lg, in);
-                step_tile<FM, FV, false, false, LG>(t, tile, c, ct, wl, in);
+                step_tile<FM, FV, false, false, LG, K1>(t, tile, c, ct, wl, in);
             }
         }
     }
@@ -1848,7 +1978,12 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __res
         const int nvalid = rem <= 0 ? 0 : (rem >= kLaneElems ? kLaneElems : (int)rem);
         if (nvalid == 0) continue;
         const int64_t gi = e0 >> lg2_group;
-        const OldGroup og = old_group(gp(s)[gi], gp(k)[gi], Fmt<F>::LOG2_FPMAX, Fmt<F>::LOG2_FPMAX_LO);
+        const double sg = gp(s)[gi];
+        const float kg = gp(k)[gi];
+        const OldGroup og = old_group(sg, kg, Fmt<F>::LOG2_FPMAX, Fmt<F>::LOG2_FPMAX_LO);
+        // k = 1: the plain product |q| s, rounded to fp32 (as the definition)
+        const bool k1 = kg == 1.0f;
+        auto k1_value = [&](uint32_t w, int i) { return (float)(code_value<F>(w, i) * sg); };
         if ((tile + 1) * kTile <= n) {
             // a whole tile: the lane's 16 values re-laid through LDS and stored
             // 4 per lane per quarter tile (each wave store 1 KB)
@@ -1857,6 +1992,12 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __res
             float out[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) out[i] = dequant_f32(w[i >> 2], i & 3, og, lq);
+            if (__builtin_expect(__any(k1), 0)) {
+                if (k1) {
+#pragma unroll 1
+                    for (int i = 0; i < 16; ++i) out[i] = k1_value(w[i >> 2], i & 3);
+                }
+            }
             const uint32_t ob = xfer_off(4 * lane_opaque());
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -1870,7 +2011,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(const uint8_t* __res
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (i < nvalid) X[e0 + i] = dequant_f32(Q[e0 + i], 0, og, lq);
+                if (i < nvalid) X[e0 + i] = k1 ? k1_value(Q[e0 + i], 0) : dequant_f32(Q[e0 + i], 0, og, lq);
         }
     }
 }
@@ -1927,20 +2068,28 @@ constexpr int kStepBlocksPerCU = 256;
 
 // Groups of 128 and more: the whole tiles run in the table kernel, then a
 // direct-path launch covers any partial tiles. Otherwise one direct-path launch.
-template <int FM, int FV>
-void launch_single(const TensorRef& t, const StepConsts& c, hipStream_t st) {
+template <int FM, int FV, bool K1>
+void launch_single_k1(const TensorRef& t, const StepConsts& c, hipStream_t st) {
     const int64_t tiles = (t.n + kTile - 1) / kTile, full = t.n / kTile;
     if (c.lg2_group >= 7) {
         if (full > 0)
-            hipLaunchKernelGGL((step_single_kernel<FM, FV, true>), dim3(grid_for(full, kStepBlocksPerCU)),
+            hipLaunchKernelGGL((step_single_kernel<FM, FV, true, K1>), dim3(grid_for(full, kStepBlocksPerCU)),
                                dim3(kBlock), 0, st, t, c, kPhaseFull);
         if (tiles > full)
-            hipLaunchKernelGGL((step_single_kernel<FM, FV, false>), dim3(1), dim3(kBlock), 0, st, t, c,
+            hipLaunchKernelGGL((step_single_kernel<FM, FV, false, K1>), dim3(1), dim3(kBlock), 0, st, t, c,
                                kPhasePartial);
         return;
     }
-    hipLaunchKernelGGL((step_single_kernel<FM, FV, false>), dim3(grid_for(tiles, kStepBlocksPerCU)), dim3(kBlock),
-                       0, st, t, c, kPhaseFull | kPhasePartial);
+    hipLaunchKernelGGL((step_single_kernel<FM, FV, false, K1>), dim3(grid_for(tiles, kStepBlocksPerCU)),
+                       dim3(kBlock), 0, st, t, c, kPhaseFull | kPhasePartial);
+}
+// Without expansion for either moment every group is stored with k = 1 after
+// the first step: the K1 kernels, which treat whole waves of such groups on
+// a path of their own.
+template <int FM, int FV>
+void launch_single(const TensorRef& t, const StepConsts& c, hipStream_t st) {
+    if (!c.expand_m && !c.expand_v) launch_single_k1<FM, FV, true>(t, c, st);
+    else launch_single_k1<FM, FV, false>(t, c, st);
 }
 
 // The multi-tensor kernels are specialized on the group size (groups of
@@ -1949,8 +2098,13 @@ void launch_single(const TensorRef& t, const StepConsts& c, hipStream_t st) {
 template <int FM, int FV, bool TAB, int LG>
 void launch_multi_lg(const TensorRef* ts, const int64_t* fb, const int32_t* partial, int count, int n_partial,
                      int64_t waves, const StepConsts& c, int phases, hipStream_t st) {
-    hipLaunchKernelGGL((step_multi_kernel<FM, FV, TAB, LG>), dim3(grid_for(waves, kStepBlocksPerCU)), dim3(kBlock),
-                       0, st, ts, fb, partial, count, n_partial, c, phases);
+    // K1 kernels for launches without expansion (see launch_single)
+    if (!c.expand_m && !c.expand_v)
+        hipLaunchKernelGGL((step_multi_kernel<FM, FV, TAB, LG, true>), dim3(grid_for(waves, kStepBlocksPerCU)),
+                           dim3(kBlock), 0, st, ts, fb, partial, count, n_partial, c, phases);
+    else
+        hipLaunchKernelGGL((step_multi_kernel<FM, FV, TAB, LG, false>), dim3(grid_for(waves, kStepBlocksPerCU)),
+                           dim3(kBlock), 0, st, ts, fb, partial, count, n_partial, c, phases);
 }
 
 template <int FM, int FV>

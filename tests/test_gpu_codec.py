@@ -102,6 +102,10 @@ def test_quantize_parity(coat, fmt, G, n):
         assert rel_err(S.cpu().numpy(), s).max() <= 1e-5
         d = code_steps(Q.cpu().numpy(), q)
         assert d.max() <= 1 and (d != 0).mean() <= 1e-4
+        if fmt & NOEXP:
+            # k = 1: s = amax / fpmax and every code exactly as the oracle's
+            assert np.array_equal(S.cpu().numpy(), s) and np.all(K.cpu().numpy() == 1.0)
+            assert np.array_equal(Q.cpu().numpy(), q)
 
 
 @pytest.mark.parametrize("fmt", [E4, E5])
@@ -154,6 +158,9 @@ def test_dequantize_every_code_and_special_groups(coat, fmt, G):
     ok = (got[fin] == want32) | (np.abs(got[fin] - want[fin]) <= np.spacing(np.abs(want[fin]).astype(np.float32)))
     assert ok.all(), np.flatnonzero(~ok)[:10]
     assert np.array_equal(np.signbit(got[fin]), np.signbit(want[fin]))
+    # k = 1: the plain product |q| s, rounded once to fp32, exactly as the oracle's
+    k1 = np.repeat(k == 1.0, G)[:n] & fin
+    assert np.array_equal(got[k1], want[k1].astype(np.float32).astype(np.float64))
 
 
 @pytest.mark.parametrize("fmt", [E4, E5])

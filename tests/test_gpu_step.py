@@ -53,8 +53,14 @@ def test_no_expansion(fm, fv):
     x = make_inputs(n, G, fm, fv, seed=31)
     got, ref = gpu_step(x), oracle_step(x)
     compare(got, ref, "noexp")
-    if fm & NOEXP:
-        assert np.all(got["mk"] == 1.0)
+    # a moment stored and requantized with k = 1 follows the definition's
+    # arithmetic exactly: s = amax / fpmax, |q| s, RN(RN(b x) + RN(c g)), so its
+    # scales and codes equal the oracle's bit for bit
+    for st, f in (("m", fm), ("v", fv)):
+        if f & NOEXP:
+            assert np.all(got[st + "k"] == 1.0)
+            assert np.array_equal(got[st + "s"], ref[st + "s"]), st
+            assert np.array_equal(got[st + "q"], ref[st + "q"]), st
 
 
 @pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 127, 128, 129, 1023, 1024, 1025, 4096 + 3])

@@ -184,6 +184,12 @@ def test_ten_steps_drift_and_ablation(coat):
                                                                  "m_code_frac", "v_code_frac")}
         log(f"  {name}: same-input parity over t = 10..19, worst {worst}")
     log(f"  median ms/step {np.median(exp['times']):.2f} (expansion), {np.median(noexp['times']):.2f} (k = 1)")
+    # with k = 1 the kernels follow the definition's arithmetic exactly: from
+    # the GPU's own state the step equals the oracle's in every scale and code,
+    # so the two chains never part
+    worst1 = {k: max(m[k] for m in noexp["same_input"]) for k in ("m_s_rel", "v_s_rel", "m_code_frac", "v_code_frac")}
+    assert all(v == 0.0 for v in worst1.values()), worst1
+    assert noexp["parted"] == 0
     # expansion keeps the states closer to unquantized AdamW
     assert exp["m"][0] < noexp["m"][0] and exp["v"][0] < noexp["v"][0]
     assert exp["m"][1] < noexp["m"][1] and exp["v"][1] < noexp["v"][1]
