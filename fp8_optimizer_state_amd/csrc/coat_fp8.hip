@@ -42,13 +42,21 @@ namespace {
 //
 // exp2: u = n + f with n = rint(u), |f| <= 1/2, and 2^f = exp(f ln 2). The
 // polynomial is the degree-10 one interpolating 2^f at the eleven Chebyshev
-// nodes of [-1/2, 1/2] (relative error below 2^-51.5), shared by every use so
-// that the kernels hold only one set of its constants (fp64 operands cannot be
-// instruction literals here; they occupy registers). The smallest member of a
+// nodes of [-1/2, 1/2] (relative error below 2^-51.5), shared by every use but
+// the direct path's per-element dequantization below, so that the kernels hold
+// few sets of constants (fp64 operands cannot be instruction literals here;
+// they occupy registers). The smallest member of a
 // group is usually a near-cancellation b1*m + (1-b1)*g whose relative error is
 // the dequantization error amplified by |b1*m| / |m'| (1e8 and more in the
 // tails of a 13e9-element step), and k and s follow it, so the dequantized
 // moments are kept within a few 1e-15.
+// The direct path's per-element dequantization splits finer: u = (32 n + j) / 32 + f with
+// |f| <= 1/64, 2^u = 2^n 2^(j/32) 2^f, the 32 values 2^(j/32) (correctly
+// rounded) from a per-block LDS table and 2^f from the degree-5 polynomial
+// interpolating it at the six Chebyshev nodes of [-1/64, 1/64] (widened by
+// 2^-12; relative error below 2^-52.6 with its fp64 coefficients). Evaluated
+// in fp64 the whole product is as accurate as the degree-10 form (about 2^-51
+// at worst) for half the polynomial.
 // log2: x = m 2^e with m in [sqrt(1/2), sqrt(2)), u = (m-1)/(m+1), and
 // ln m = 2 atanh(u) = 2 sum u^(2j+1) / (2j+1); |u| <= 0.1716, so 12 terms
 // reach 2^-56. Quotients and reciprocals use the hardware reciprocal estimate
@@ -63,6 +71,21 @@ __device__ constexpr double kExp2C[kExp2N] = {
     0x1.e6063f7217bc6p-28, 0x1.b675bca4eeebbp-24, 0x1.62bfd47773353p-20, 0x1.ffcb54062e698p-17,
     0x1.430913096fd9fp-13, 0x1.5d87fe9d7a584p-10, 0x1.3b2ab6fba1ddap-7,  0x1.c6b08d703ce49p-5,
     0x1.ebfbdff82c598p-3,  0x1.62e42fefa3a19p-1,  1.0};
+// 2^f on [-1/64, 1/64] (degree 5, highest first) and 2^(j/32), j = 0..31.
+constexpr int kExp2SN = 6;
+__device__ constexpr double kExp2SC[kExp2SN] = {
+    0x1.5d885e7af0753p-10, 0x1.3b2b302e43a47p-7, 0x1.c6b08d7038095p-5, 0x1.ebfbdff7fee04p-3,
+    0x1.62e42fefa39efp-1,  1.0};
+constexpr int kExp2J = 32;
+__device__ constexpr double kExp2JT[kExp2J] = {
+    0x1.0000000000000p+0, 0x1.059b0d3158574p+0, 0x1.0b5586cf9890fp+0, 0x1.11301d0125b51p+0,
+    0x1.172b83c7d517bp+0, 0x1.1d4873168b9aap+0, 0x1.2387a6e756238p+0, 0x1.29e9df51fdee1p+0,
+    0x1.306fe0a31b715p+0, 0x1.371a7373aa9cbp+0, 0x1.3dea64c123422p+0, 0x1.44e086061892dp+0,
+    0x1.4bfdad5362a27p+0, 0x1.5342b569d4f82p+0, 0x1.5ab07dd485429p+0, 0x1.6247eb03a5585p+0,
+    0x1.6a09e667f3bcdp+0, 0x1.71f75e8ec5f74p+0, 0x1.7a11473eb0187p+0, 0x1.82589994cce13p+0,
+    0x1.8ace5422aa0dbp+0, 0x1.93737b0cdc5e5p+0, 0x1.9c49182a3f090p+0, 0x1.a5503b23e255dp+0,
+    0x1.ae89f995ad3adp+0, 0x1.b7f76f2fb5e47p+0, 0x1.c199bdd85529cp+0, 0x1.cb720dcef9069p+0,
+    0x1.d5818dcfba487p+0, 0x1.dfc97337b9b5fp+0, 0x1.ea4afa2a490dap+0, 0x1.f50765b6e4540p+0};
 __device__ constexpr double kLog2C[kLog2N] = {
     0x1.00ecd7e080215p-3, 0x1.1964ec6fc9491p-3, 0x1.3703c1f4d0ffep-3, 0x1.5b9ac9b743f0dp-3,
     0x1.89f3b1694cffep-3, 0x1.c68f568d31760p-3, 0x1.0c9a84994022dp-2, 0x1.484b13d7c02a9p-2,
@@ -88,10 +111,23 @@ __device__ __forceinline__ double fma3(double a, double b, double c) {
     return r;
 }
 
+// a * b + c with the constant b in a scalar register.
+__device__ __forceinline__ double fma3b(double a, double b, double c) {
+    double r;
+    asm("v_fma_f64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ double exp2_poly10(double f) {
     double p = kExp2C[0];
 #pragma unroll
     for (int i = 1; i < kExp2N; ++i) p = fma3(p, f, kExp2C[i]);
+    return p;
+}
+__device__ __forceinline__ double exp2_poly5(double f) {
+    double p = kExp2SC[0];
+#pragma unroll
+    for (int i = 1; i < kExp2SN; ++i) p = fma3(p, f, kExp2SC[i]);
     return p;
 }
 __device__ __forceinline__ double exp2_poly10(double f, CoefPtr cf) {
@@ -224,10 +260,11 @@ __device__ __forceinline__ double group_min(double v, int lanes) {
 }
 
 // Per-block constant tables, one row per moment:
-//   lqb[c] = for each of the 256 codes, lq = log2(value(c & 0x7F) / fpmax), the
-//            per-code constant of the dequantization |x| = A 2^(lq / k) (zero
-//            maps to -1e300 and Inf to +1e300 so that the same arithmetic yields
-//            0 and Inf, NaN codes to NaN), and b = the moment's decay with the
+//   lqb[c] = for each of the 256 codes, lq = 32 log2(value(c & 0x7F) / fpmax),
+//            the per-code constant of the dequantization |x| = A 2^(lq / 32k)
+//            (scaled by 32 for the split of the exponent into 32nds; zero maps
+//            to -1e300 and Inf to +1e300 so that the same arithmetic yields 0
+//            and Inf, NaN codes to NaN), and b = the moment's decay with the
 //            code's sign (the step's first operation on the dequantized value
 //            is b x; the codec kernels use b = 1);
 //   lqm[c] = log2(midpoint(c, c+1) / fpmax), the per-code constant of the
@@ -264,8 +301,9 @@ struct DirectTables {
     LqEntry lqb[2][256];
     double lqm[2][128];
     double coef[kCoefN];
+    double e32[kExp2J];    // 2^(j/32)
 };
-// Tables of the table path: lq without the sign and decay (only its rare
+// Tables of the table path: lq (unscaled) without the sign and decay (only its rare
 // exact paths dequantize code by code), the per-code table offsets and the
 // builder lanes' jobs.
 struct TabTables {
@@ -292,7 +330,9 @@ __device__ __forceinline__ CoefPtr coef_ptr(const double* coef) {
 // The dequantization constants of a code, with the sign and decay folded into
 // tb (direct path: from the 256-entry table) ...
 struct LqSigned {
+    static constexpr bool kSplit32 = true;
     const LqEntry* t;
+    const double* e32;
     __device__ double get(uint32_t c, double& tb) const {
         const LqEntry e = t[c];
         tb = e.b;
@@ -301,6 +341,7 @@ struct LqSigned {
 };
 // ... or with tb formed from the code's sign (table path).
 struct LqSplit {
+    static constexpr bool kSplit32 = false;
     const double* lq;
     double b;
     __device__ double get(uint32_t c, double& tb) const {
@@ -434,13 +475,14 @@ __device__ void table_jobs(TableJobs& j, int tid) {
 template <int FM, int FV>
 __device__ __forceinline__ void fill_direct_tables(DirectTables& ct, double bm, double bv) {
     const int f = threadIdx.x >> 7, c = threadIdx.x & 127;
-    const double lq = f ? lq_entry<FV>(c) : lq_entry<FM>(c);
+    const double lq = 32.0 * (f ? lq_entry<FV>(c) : lq_entry<FM>(c));
     const double b = f ? bv : bm;
     ct.lqb[f][c] = LqEntry{lq, b};
     ct.lqb[f][c | 128] = LqEntry{lq, -b};
     ct.lqm[f][c] = f ? lqm_entry<FV>(c) : lqm_entry<FM>(c);
     if (threadIdx.x < kCoefN)
         ct.coef[threadIdx.x] = threadIdx.x < kExp2N ? kExp2C[threadIdx.x] : kLog2C[threadIdx.x - kExp2N];
+    if (threadIdx.x < kExp2J) ct.e32[threadIdx.x] = kExp2JT[threadIdx.x];
     __syncthreads();
 }
 
@@ -708,12 +750,27 @@ static_assert(kTile == kPlanTile, "tile size of the plan tables");
 // Dequantize byte i of code word w: returns the magnitude
 // 2^(LQ[c] r + a + a_lo) and sets tb to the code's table factor (+/- b), so
 // that the signed value times b is tb * magnitude.
+// Direct path (every element goes through here): the table holds 32 LQ, so
+// U = fma(32 LQ, r, 32 a) = 32 u exactly (scaling by a power of two commutes
+// with the rounding); with N = rint(U), U - N is exact (the two are within 1/2
+// of each other, or N = 0), 2^u = 2^(N >> 5) 2^((N & 31) / 32) 2^((U - N) / 32).
+// A NaN u gives N = 0 and a NaN result; a huge |u| saturates N, and the power
+// of two then flushes to 0 or Inf. Table path (only its rare exact branches
+// come here): 2^u = 2^rint(u) 2^(u - rint(u)) with the degree-10 polynomial.
 template <typename L>
 __device__ __forceinline__ double dequant_mag(uint32_t w, int i, const OldGroup& og, const L& src, double& tb) {
     const double lq = src.get((w >> (8 * i)) & 0xFFu, tb);
-    const double u = __builtin_fma(lq, og.r, og.a);
-    const double n = __builtin_rint(u);
-    return __builtin_amdgcn_ldexp(exp2_poly10((u - n) + og.a_lo), cvt_i32_sat(n));
+    if constexpr (L::kSplit32) {
+        const double u32 = __builtin_fma(lq, og.r, og.a * 32.0);
+        const double n32 = __builtin_rint(u32);
+        const int ni = cvt_i32_sat(n32);
+        const double f = fma3b(u32 - n32, 0x1p-5, og.a_lo);
+        return __builtin_amdgcn_ldexp(src.e32[ni & 31] * exp2_poly5(f), ni >> 5);
+    } else {
+        const double u = __builtin_fma(lq, og.r, og.a);
+        const double n = __builtin_rint(u);
+        return __builtin_amdgcn_ldexp(exp2_poly10((u - n) + og.a_lo), cvt_i32_sat(n));
+    }
 }
 
 
@@ -1150,7 +1207,9 @@ __device__ __forceinline__ EntryPair table_entries(uint32_t e, const GroupTable&
 // split over lane pairs (group >= 32), so no lane needs a bounds check.
 // LG: log2 of the group size when fixed at compile time (0: c.lg2_group), so
 // that the lane-group reductions unroll into straight DPP sequences.
-__device__ __forceinline__ LqSigned lq_source(const DirectTables& ct, int f, double) { return LqSigned{ct.lqb[f]}; }
+__device__ __forceinline__ LqSigned lq_source(const DirectTables& ct, int f, double) {
+    return LqSigned{ct.lqb[f], ct.e32};
+}
 __device__ __forceinline__ LqSplit lq_source(const TabTables& ct, int f, double b) { return LqSplit{ct.lq[f], b}; }
 
 // The dequantization constants of both moments from the park area (rare
