@@ -55,8 +55,8 @@ namespace {
 // rounded) from a per-block LDS table and 2^f from the degree-5 polynomial
 // interpolating it at the six Chebyshev nodes of [-1/64, 1/64] (widened by
 // 2^-12; relative error below 2^-52.6 with its fp64 coefficients). Evaluated
-// in fp64 the whole product is as accurate as the degree-10 form (about 2^-51
-// at worst) for half the polynomial.
+// in fp64 the whole product is within 2^-50.3 of 2^u at worst (2^-51.0 for the
+// degree-10 form) for half the polynomial.
 // log2: x = m 2^e with m in [sqrt(1/2), sqrt(2)), u = (m-1)/(m+1), and
 // ln m = 2 atanh(u) = 2 sum u^(2j+1) / (2j+1); |u| <= 0.1716, so 12 terms
 // reach 2^-56. Quotients and reciprocals use the hardware reciprocal estimate
@@ -124,11 +124,19 @@ __device__ __forceinline__ double exp2_poly10(double f) {
     for (int i = 1; i < kExp2N; ++i) p = fma3(p, f, kExp2C[i]);
     return p;
 }
-__device__ __forceinline__ double exp2_poly5(double f) {
-    double p = kExp2SC[0];
+// 2^(d/32 + l) for |d| <= 1/2 and a small l (the low part of the exponent):
+// the degree-5 polynomial above in f = d / 32, its coefficients scaled by
+// 32^-i (exact) so that d enters unscaled, and its constant term replaced by
+// c0 = 1 + l ln 2. That drops l ln 2 (2^f - 1), at most |l| 2^-7 relative:
+// 2^-51 for |l| = 2^-44, the low part's size for exponents near 2^8 in
+// magnitude, far less for common ones.
+__device__ constexpr double kExp2SD[kExp2SN - 1] = {
+    kExp2SC[0] * 0x1p-25, kExp2SC[1] * 0x1p-20, kExp2SC[2] * 0x1p-15, kExp2SC[3] * 0x1p-10, kExp2SC[4] * 0x1p-5};
+__device__ __forceinline__ double exp2_poly5_32(double d, double c0) {
+    double p = kExp2SD[0];
 #pragma unroll
-    for (int i = 1; i < kExp2SN; ++i) p = fma3(p, f, kExp2SC[i]);
-    return p;
+    for (int i = 1; i < kExp2SN - 1; ++i) p = fma3(p, d, kExp2SD[i]);
+    return __builtin_fma(p, d, c0);
 }
 __device__ __forceinline__ double exp2_poly10(double f, CoefPtr cf) {
     double p = cf[kCoefExp2];
@@ -764,8 +772,8 @@ __device__ __forceinline__ double dequant_mag(uint32_t w, int i, const OldGroup&
         const double u32 = __builtin_fma(lq, og.r, og.a * 32.0);
         const double n32 = __builtin_rint(u32);
         const int ni = cvt_i32_sat(n32);
-        const double f = fma3b(u32 - n32, 0x1p-5, og.a_lo);
-        return __builtin_amdgcn_ldexp(src.e32[ni & 31] * exp2_poly5(f), ni >> 5);
+        const double c0 = __builtin_fma(og.a_lo, 0x1.62e42fefa39efp-1, 1.0);
+        return __builtin_amdgcn_ldexp(src.e32[ni & 31] * exp2_poly5_32(u32 - n32, c0), ni >> 5);
     } else {
         const double u = __builtin_fma(lq, og.r, og.a);
         const double n = __builtin_rint(u);

@@ -61,22 +61,36 @@ def test_exp2_polynomial_error(name, h, bound):
 
 
 def test_split_reproduces_exp2():
-    """2^u = 2^(N >> 5) 2^((N & 31) / 32) 2^((U - N) / 32) with U = 32 u,
-    N = rint(U), evaluated as the direct path does (fp64 steps, fma where it
-    uses one), within 2^-50.5 of 2^u on a spread of u, negatives included."""
+    """2^(u + l) = 2^(N >> 5) 2^((N & 31) / 32) 2^((U - N) / 32) 2^l with
+    U = 32 u, N = rint(U) and l a small low part, evaluated as the direct path
+    does: the polynomial in d = U - N with its coefficients scaled by 32^-i and
+    its constant term 1 + l ln 2 (which drops l ln 2 (2^f - 1), at most
+    |l| 2^-7 relative). Within 2^-50.3 of 2^(u + l) on a spread of u
+    (negatives included) and |l| up to 2^-44, the low part's size for |u|
+    near 2^8; within 2^-50.9 for |l| up to 2^-47."""
     import numpy as np
     mp.mp.prec = 200
     t = np.array(_array("kExp2JT"))
     c = _array("kExp2SC")
+    deg = len(c) - 1
+    cd = [c[i] * 2.0 ** (-5 * (deg - i)) for i in range(deg)]  # highest degree first, without the constant
     rng = np.random.default_rng(5)
     u = np.concatenate([rng.uniform(-60, 60, 400), rng.uniform(-0.05, 0.05, 200), [0.0, -1 / 64, 1 / 64, 31 / 32]])
+    for lo_max, bound in ((2.0 ** -44, -50.3), (2.0 ** -47, -50.9)):
+        _check_split(t, cd, u, rng.uniform(-1, 1, u.size) * lo_max, bound)
+
+
+def _check_split(t, cd, u, lo, bound):
+    import numpy as np
     U = u * 32.0
     N = np.rint(U)
-    f = (U - N) * 2.0 ** -5
-    p = np.full_like(f, c[0])
-    for ci in c[1:]:
-        p = p * f + ci
+    d = U - N
+    p = np.full_like(d, cd[0])
+    for ci in cd[1:]:
+        p = p * d + ci
+    p = p * d + (1.0 + lo * float.fromhex("0x1.62e42fefa39efp-1"))
     Ni = N.astype(np.int64)
     y = np.ldexp(t[Ni & 31] * p, Ni >> 5)
-    worst = max(abs(mp.mpf(float(yi)) / mp.power(2, mp.mpf(float(ui))) - 1) for yi, ui in zip(y, u))
-    assert float(mp.log(worst, 2)) < -50.5
+    worst = max(abs(mp.mpf(float(yi)) / mp.power(2, mp.mpf(float(ui)) + mp.mpf(float(li))) - 1)
+                for yi, ui, li in zip(y, u, lo))
+    assert float(mp.log(worst, 2)) < bound
