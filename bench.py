@@ -13,9 +13,10 @@ With --ceiling it measures, in one process and on the same resident
 workload, what the step's time is judged against: a plain device copy of
 4 GiB (torch copy_), the memory-only floor of the step's access pattern (the
 instrument in bench_ceiling.hip: the step's bytes in the step's pattern, no
-arithmetic) at the step's residency and at full residency, and the step
-itself, in interleaved rounds; one JSON line per measurement and round, a
-markdown table on stderr.
+arithmetic) at the step's residency and at full residency, the step
+without expansion (every group k = 1: the same bytes, the least arithmetic)
+and the step itself, in interleaved rounds; one JSON line per measurement and
+round, a markdown table on stderr.
 
 With --sweep it instead times the step and measures the state codec's
 quantization error for every group size in {32, 64, 128, 256}, format pair
@@ -368,8 +369,9 @@ def ceiling(args) -> int:
                                         stream.cuda_stream)
         assert rc == 0, rc
 
-    def step_once():
-        st.step(step=step_no[0], **hy)
+    def step_once(expand=True):
+        flag = 0 if expand else coat.FMT_NO_EXPAND
+        st.step(step=step_no[0], **dict(hy, fmt_m=wl.fmt_m | flag, fmt_v=wl.fmt_v | flag))
         step_no[0] += 1
 
     # plain streams over 4 GiB buffers (copy: 4 GiB read + 4 GiB written)
@@ -391,7 +393,11 @@ def ceiling(args) -> int:
              ("pattern floor, whole-tile (the step's), step residency", lambda: probe_pass(1, step_lds),
               bpp * n_probe),
              ("pattern floor, whole-tile, full residency", lambda: probe_pass(1, 0), bpp * n_probe),
+             ("step without expansion (k = 1)", lambda: step_once(False), bpp * wl.n_params),
              ("step", step_once, bpp * wl.n_params))
+    # the two step rows leave the state in each other's form (k = 1 or
+    # expanded), so each timed batch of a step row follows one untimed launch
+    primed = {"step without expansion (k = 1)", "step"}
     for _, fn, _ in kinds:
         for _ in range(args.warmup):
             fn()
@@ -405,6 +411,8 @@ def ceiling(args) -> int:
         print(json.dumps({"ceiling": "copy 4 GiB (torch copy_)", "round": r, "ms": ms, "GBps": gbps,
                           "frac_of_8TBps": gbps / PEAK_HBM_GBPS}), flush=True)
         for name, fn, nbytes in kinds:
+            if name in primed:
+                fn()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(args.steps):
