@@ -7,7 +7,13 @@ resident in HBM (about 133 GB). One step = one multi-tensor launch over the
 whole list. Prints one JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama13b]
-                  [--no-cpu-baseline] [--copy-calibration] [--sweep | --act | --codec | --ceiling]
+                  [--no-cpu-baseline] [--no-reference] [--copy-calibration]
+                  [--sweep | --act | --codec | --ceiling]
+
+After the measured steps it also times, unless --no-reference, the same step
+without expansion (every group k = 1: the same bytes with the least
+arithmetic) on the same box, as a reference for what the box's memory and
+clock allow; it is reported beside the measurement, never as `value`.
 
 With --ceiling it measures, in one process and on the same resident
 workload, what the step's time is judged against: a plain device copy of
@@ -487,6 +493,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama13b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip the step without expansion timed after the measured steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
     ap.add_argument("--sweep", action="store_true",
@@ -558,6 +566,35 @@ def main() -> int:
     ms_median, ms_min = per_step[len(per_step) // 2], per_step[0]
     log(f"timed {args.steps} steps: {ms:.3f} ms/step (median {ms_median:.3f}, min {ms_min:.3f})")
 
+    n = wl.n_params
+    bpp = wl.bytes_per_param()
+    launch_bytes = bpp * n
+
+    # the same step without expansion, after the measured steps (which it
+    # does not touch): warm-up launches first, the first of which converts the
+    # state to k = 1 groups
+    ref = None
+    if not args.no_reference:
+        noexp = dict(hy, fmt_m=wl.fmt_m | coat.FMT_NO_EXPAND, fmt_v=wl.fmt_v | coat.FMT_NO_EXPAND)
+        for _ in range(max(args.warmup, 1)):
+            st.step(step=step, **noexp)
+            step += 1
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        r0.record(stream)
+        for _ in range(args.steps):
+            st.step(step=step, **noexp)
+            step += 1
+        r1.record(stream)
+        torch.cuda.synchronize()
+        ref_ms = r0.elapsed_time(r1) / args.steps
+        ref_gbps = launch_bytes / (ref_ms * 1e-3) / 1e9
+        ref = {"what": "the same step with COAT_FMT_NO_EXPAND on both moments (every group k = 1: "
+                       "the same bytes, no 2^x, no per-group tables), timed after the measured steps",
+               "ms_per_step": ref_ms, "GBps": ref_gbps, "frac_of_8TBps": ref_gbps / PEAK_HBM_GBPS,
+               "measured_over_reference_time": ms / ref_ms}
+        log(f"reference without expansion: {ref_ms:.3f} ms/step ({100 * ref_gbps / PEAK_HBM_GBPS:.1f} % of 8 TB/s)")
+
     copy = None
     if args.copy_calibration:
         # a device copy of known size, for the counter calibration, timed as well
@@ -566,9 +603,6 @@ def main() -> int:
                 "frac_of_8TBps": copy_gbps / PEAK_HBM_GBPS}
         log(f"copy calibration: 4 GiB fp32 copy, {copy_ms:.3f} ms, {copy_gbps:.0f} GB/s")
 
-    n = wl.n_params
-    bpp = wl.bytes_per_param()
-    launch_bytes = bpp * n
     achieved = launch_bytes / (ms * 1e-3) / 1e9
     traffic = load_traffic(args.workload, launch_bytes)
 
@@ -617,6 +651,8 @@ def main() -> int:
         },
         "cpu_baseline": cpu,
     }
+    if ref is not None:
+        out["reference_no_expansion"] = ref
     if copy is not None:
         out["copy_calibration"] = copy
     print(json.dumps(out), flush=True)
