@@ -10,7 +10,7 @@ import synth
 from _parity import HYPER, bf16_bits, compare, log
 
 pytestmark = pytest.mark.gpu
-E4, E5 = 0, 1
+E4, E5, NOEXP = 0, 1, 0x100
 
 
 @pytest.fixture(scope="module")
@@ -103,6 +103,41 @@ def test_mixed_list_equals_single_calls(coat, G, fm, fv):
             assert np.array_equal(x[key], y[key], equal_nan=True), key
     ref = oracle_list([h for h, n in zip(host, sizes) if n], G, fm, fv)
     compare(concat([x for x, n in zip(a, sizes) if n]), concat(ref), f"mixed-list G={G}")
+
+
+@pytest.mark.parametrize("G,fm,fv", [(128, E4 | NOEXP, E5 | NOEXP), (256, E4 | NOEXP, E4 | NOEXP),
+                                     (32, E4 | NOEXP, E4 | NOEXP), (64, E4 | NOEXP, E5 | NOEXP),
+                                     (128, E4 | NOEXP, E5), (32, E4, E4 | NOEXP)])
+def test_mixed_list_without_expansion(coat, G, fm, fv):
+    """The multi-tensor kernels specialized for launches without expansion
+    (every group stored with k = 1; the table kernel for G >= 128, the direct
+    kernel below) and the expanded kernels with one moment at k = 1: the same
+    list as above, bit-identical to single-tensor calls, within tolerance of
+    the oracle, and each moment without expansion equal to the oracle's in
+    every scale and code."""
+    sizes = [768, 0, 1, 17, 2304, 1024 * 5 + 3, 50, 128 * 33, 4096 + 1000, 16, 1024 * 9 + 512 + 7]
+    log(f"test_mixed_list_without_expansion G={G} fm={fm:#x} fv={fv:#x}")
+    st, host = build_list(coat, sizes, G, fm, fv, seed=43)
+    st2, _ = build_list(coat, sizes, G, fm, fv, seed=43)
+    st.step(**step_kwargs(fm, fv))
+    for i in range(len(sizes)):
+        t = st2.tensor(i)
+        if sizes[i]:
+            coat.adamw_step(t.params, t.params_bf16, t.grads, t.m_q, t.m_s, t.m_k, t.v_q, t.v_s, t.v_k,
+                            group=G, **step_kwargs(fm, fv))
+    torch.cuda.synchronize()
+    a, b = read_list(st), read_list(st2)
+    for x, y in zip(a, b):
+        for key in x:
+            assert np.array_equal(x[key], y[key], equal_nan=True), key
+    got = concat([x for x, n in zip(a, sizes) if n])
+    ref = concat(oracle_list([h for h, n in zip(host, sizes) if n], G, fm, fv))
+    compare(got, ref, f"mixed-list no expansion G={G}")
+    for mo, f in (("m", fm), ("v", fv)):
+        if f & NOEXP:
+            assert np.all(got[mo + "k"] == 1.0), mo
+            assert np.array_equal(got[mo + "s"], ref[mo + "s"]), mo
+            assert np.array_equal(got[mo + "q"], ref[mo + "q"]), mo
 
 
 def test_unplanned_entry_point(coat):
