@@ -111,13 +111,6 @@ __device__ __forceinline__ double fma3(double a, double b, double c) {
     return r;
 }
 
-// a * b + c with the constant b in a scalar register.
-__device__ __forceinline__ double fma3b(double a, double b, double c) {
-    double r;
-    asm("v_fma_f64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "v"(c));
-    return r;
-}
-
 __device__ __forceinline__ double exp2_poly10(double f) {
     double p = kExp2C[0];
 #pragma unroll
