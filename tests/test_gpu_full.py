@@ -10,6 +10,7 @@ every group of the first transformer block, and every 997th group. An
 opt-in denser run (test_full_size_dense) takes every N-th group instead, N
 from the environment variable COAT_DENSE_PARITY (e.g. 97).
 """
+import dataclasses
 import os
 import time
 from concurrent.futures import ThreadPoolExecutor
@@ -110,9 +111,11 @@ def concat(lst):
     return {k: np.concatenate([d[k] for d in lst]) for k in lst[0]}
 
 
-def run_full(coat, name, every=997):
-    """One planned step over the whole list; the sampled groups against the oracle."""
-    wl = synth.WORKLOADS[name]
+def run_full(coat, name, every=997, outputs=False):
+    """One planned step over the whole list; the sampled groups against the oracle.
+    `name` is a workload name or a synth.Workload."""
+    wl = synth.WORKLOADS[name] if isinstance(name, str) else name
+    name = wl.name
     dev = torch.device("cuda")
     sample = synth.parity_sample(wl, every=every)
     n_groups = sum(len(ix) for _, ix in sample)
@@ -140,13 +143,28 @@ def run_full(coat, name, every=997):
         log(f"  {m}: groups {len(g[m + 'k'])}, k identical in {int(np.sum(g[m + 'k'] == r[m + 'k']))}, "
             f"k rel max {met[m + '_k_rel']:.3g}, s rel max {met[m + '_s_rel']:.3g}, "
             f"codes differing {int(np.sum(g[m + 'q'] != r[m + 'q']))}")
-    return met
+    return (met, g, r) if outputs else met
 
 
 @pytest.mark.parametrize("name", ["llama13b", "llama7b", "llama13b_g32"])
 def test_full_size_sampled(coat, name):
     met = run_full(coat, name)
     assert met["m_k_rel"] < 1e-6 and met["v_k_rel"] < 1e-6
+
+
+def test_full_size_sampled_without_expansion(coat):
+    """The 13B list with both moments without expansion (prior stored with
+    k = 1, COAT_FMT_NO_EXPAND in the step: the launch specialized for k = 1,
+    which bench.py also times as its reference): on the sampled groups every
+    k is 1 and every scale and code equals the oracle's bit for bit."""
+    base = synth.WORKLOADS["llama13b"]
+    wl = dataclasses.replace(base, name=base.name + ", no expansion", fmt_m=base.fmt_m | 0x100,
+                             fmt_v=base.fmt_v | 0x100)
+    met, g, r = run_full(coat, wl, outputs=True)
+    for m in ("m", "v"):
+        assert np.all(g[m + "k"] == 1.0), m
+        assert np.array_equal(g[m + "s"], r[m + "s"]), m
+        assert np.array_equal(g[m + "q"], r[m + "q"]), m
 
 
 @pytest.mark.skipif(not os.environ.get("COAT_DENSE_PARITY"),
