@@ -400,6 +400,8 @@ constexpr int ts_base() { return F == COAT_FMT_E4M3 ? 17 : 32; }
 template <int F>
 constexpr int te_special() { return F == COAT_FMT_E4M3 ? 16 : 31; }
 constexpr int kE5TsNan = 16;
+// k1_tables writes the special exponent entry at index nte (16 and 31)
+static_assert(te_special<COAT_FMT_E4M3>() == 16 && te_special<COAT_FMT_E5M2>() == 31, "special TE entries");
 template <int F>
 __device__ uint32_t lut_entry(int code) {
     using T = Fmt<F>;
@@ -1151,12 +1153,15 @@ __device__ __forceinline__ void build_tables(WaveLdsTab& wl, const TabTables& ct
     asm volatile("" ::: "memory");
 }
 
-// The tables of a moment stored with k = 1, rebuilt by the same builder lanes
-// after build_tables: TE[e] = 2^(max(e,1) - BIAS - MB) exactly and
-// TS[+-i] = +-RN(b RN(i s)), so that a code's TE TS, an exact product, is
-// RN(b RN(|q| s)) and the element pass's fma(TE, TS, c g) forms
-// RN(RN(b x) + RN(c g)), the definition's two roundings (see k1_moment).
-// The special entries (NaN, Inf) stay as built.
+// The tables of a moment stored with k = 1, built by the same builder lanes
+// (after build_tables, or alone in a wave whose groups all have k = 1):
+// TE[e] = 2^(max(e,1) - BIAS - MB) exactly and TS[+-i] = +-RN(b RN(i s)), so
+// that a code's TE TS, an exact product, is RN(b RN(|q| s)) and the element
+// pass's fma(TE, TS, c g) forms RN(RN(b x) + RN(c g)), the definition's two
+// roundings (see k1_moment). The special entries are written here as well
+// (E4M3: the NaN exponent entry; E5M2: the Inf exponent entry and the NaN
+// significand entry), since a wave that builds only these tables reuses LDS
+// that held other data: NaN codes must decode to NaN and Inf codes to Inf.
 template <int FM, int FV>
 __device__ __forceinline__ void k1_tables(WaveLdsTab& wl, int lpg, double s, float k, double b1, double b2) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -1176,6 +1181,11 @@ __device__ __forceinline__ void k1_tables(WaveLdsTab& wl, int lpg, double s, flo
         const double v = b * ((double)i * s);
         g[tsb + i] = v;
         g[tsb + i + nts] = -v;
+    }
+    if (t == 3) {
+        // te_special(F) is nte in both formats
+        g[nte] = e4 ? __builtin_nan("") : __builtin_inf();
+        if (!e4) g[tsb + kE5TsNan] = __builtin_nan("");
     }
     asm volatile("" ::: "memory");
 }

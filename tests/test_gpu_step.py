@@ -84,28 +84,35 @@ def test_no_bf16_copy():
     compare(got, ref, "no-bf16", check_w=False)
 
 
-def test_zero_state_and_zero_grads():
+# the rare-path tests run with expansion and, through the kernels specialized
+# for it, without expansion on both moments
+RARE_FMTS = [(E4, E5), (E4 | NOEXP, E5 | NOEXP)]
+
+
+@pytest.mark.parametrize("fm,fv", RARE_FMTS)
+def test_zero_state_and_zero_grads(fm, fv):
     """All-zero groups (zero state, zero grads) next to ordinary ones."""
     n, G = 1024 * 4, 128
-    x = make_inputs(n, G, E4, E5, seed=12)
+    x = make_inputs(n, G, fm, fv, seed=12)
     x.g[: 3 * G] = 0
     for q, s in ((x.mq, x.ms), (x.vq, x.vs)):
         q[: 3 * G] = 0
         s[:3] = 0.0
     x.g[3 * G: 3 * G + 5] = 0x8000  # -0.0 grads in an ordinary group
-    log("test_zero_state_and_zero_grads")
+    log(f"test_zero_state_and_zero_grads fm={fm:#x} fv={fv:#x}")
     got, ref = gpu_step(x), oracle_step(x)
     compare(got, ref, "zeros")
     assert np.all(got["ms"][:3] == 0) and np.all(got["mk"][:3] == 1)
 
 
-def test_nonfinite_grads_poison_their_group_only():
+@pytest.mark.parametrize("fm,fv", [(E4, E4), (E4 | NOEXP, E4 | NOEXP)])
+def test_nonfinite_grads_poison_their_group_only(fm, fv):
     n, G = 1024 * 3, 128
-    x = make_inputs(n, G, E4, E4, seed=13)
+    x = make_inputs(n, G, fm, fv, seed=13)
     x.g[5] = 0x7FC0            # NaN in group 0
     x.g[G * 7 + 3] = 0x7F80    # +Inf in group 7
     x.g[G * 12 + 100] = 0xFF80  # -Inf in group 12
-    log("test_nonfinite_grads_poison_their_group_only")
+    log(f"test_nonfinite_grads_poison_their_group_only fm={fm:#x} fv={fv:#x}")
     got, ref = gpu_step(x), oracle_step(x)
     compare(got, ref, "poison")
     for gi in (0, 7, 12):
@@ -237,36 +244,59 @@ def test_near_constant_threshold():
     assert np.array_equal(got["mk"][:5], ref["mk"][:5])
 
 
+@pytest.mark.parametrize("fm,fv", RARE_FMTS)
 @pytest.mark.parametrize("G", [16, 32, 128])
-def test_huge_grads_update_in_fp64(G):
+def test_huge_grads_update_in_fp64(G, fm, fv):
     """bf16 grads of 1e20 and up make v' (and, near the bf16 maximum, the
     update's intermediates) exceed the fp32 range while every moment stays
     finite in fp64: the update must still follow the oracle, and no group is
     poisoned."""
     n = 1024 * 3
-    x = make_inputs(n, G, E4, E5, seed=42 + G)
+    x = make_inputs(n, G, fm, fv, seed=42 + G)
     big = np.array([1e20, -3e20, 3e38, -3.3e38, 2e25], np.float32)
     x.g[5:10] = _bf16_bits(big)                # one group with several huge grads
     x.g[G + 17] = _bf16_bits(np.float32(-1e30))[()]
     x.g[1024 + 3 * G: 1024 + 4 * G] = _bf16_bits(np.full(G, 7e21, np.float32))  # a whole group
-    log(f"test_huge_grads_update_in_fp64 G={G}")
+    log(f"test_huge_grads_update_in_fp64 G={G} fm={fm:#x} fv={fv:#x}")
     got, ref = gpu_step(x), oracle_step(x)
     assert np.isfinite(ref["ms"]).all() and np.isfinite(ref["vs"]).all()
     compare(got, ref, f"huge grads G={G}")
 
 
+@pytest.mark.parametrize("G", [32, 128, 256])
+def test_nan_and_inf_codes_without_expansion(G):
+    """A state stored with k = 1 everywhere (both moments without expansion)
+    whose finite groups hold an E4M3 NaN code (first moment) or an E5M2 Inf
+    or NaN code (second moment) among ordinary codes: each such code decodes
+    to NaN or Inf as the oracle's does, in every launch shape (for G >= 128
+    the waves whose groups all have k = 1 build only the exact tables)."""
+    n = 1024 * 3
+    fm, fv = E4 | NOEXP, E5 | NOEXP
+    x = make_inputs(n, G, fm, fv, seed=44 + G)
+    assert np.all(x.mk == 1.0) and np.all(x.vk == 1.0)
+    x.mq[G + 5] = 0x7F                        # E4M3 NaN in group 1
+    x.mq[1024 + 2 * G + 9] = 0xFF             # E4M3 -NaN in a later tile
+    x.vq[3 * G + 1] = 0x7C                    # E5M2 +Inf in group 3
+    x.vq[2048 + 7] = 0x7E                     # E5M2 NaN in the last tile
+    log(f"test_nan_and_inf_codes_without_expansion G={G}")
+    got, ref = gpu_step(x), oracle_step(x)
+    compare(got, ref, f"nan/inf codes G={G}")
+    assert np.isnan(ref["p"][G + 5]) and np.isnan(got["p"][G + 5])
+
+
+@pytest.mark.parametrize("fm,fv", RARE_FMTS)
 @pytest.mark.parametrize("G", [16, 32, 128])
-def test_poisoned_state_poisons_its_own_moment_only(G):
+def test_poisoned_state_poisons_its_own_moment_only(G, fm, fv):
     """A stored first-moment group that is poisoned (s = NaN, codes 0x7F)
     next to a finite second-moment group: the first moment stays poisoned,
     the second is requantized as usual, and vice versa."""
     n = 1024 * 2
-    x = make_inputs(n, G, E4, E5, seed=43 + G)
+    x = make_inputs(n, G, fm, fv, seed=43 + G)
     x.mq[0:G] = 0x7F
     x.ms[0], x.mk[0] = np.nan, 1.0
     x.vq[3 * G:4 * G] = 0x7F                  # E5M2 NaN code
     x.vs[3], x.vk[3] = np.nan, 1.0
-    log(f"test_poisoned_state_poisons_its_own_moment_only G={G}")
+    log(f"test_poisoned_state_poisons_its_own_moment_only G={G} fm={fm:#x} fv={fv:#x}")
     got, ref = gpu_step(x), oracle_step(x)
     assert np.isnan(ref["ms"][0]) and np.isfinite(ref["vs"][0])
     assert np.isnan(ref["vs"][3]) and np.isfinite(ref["ms"][3])
