@@ -2135,6 +2135,21 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const uint8_t* __restric
 // blocks the 13B step takes 10 % longer); beyond a few hundred per CU each
 // block's table set-up starts to cost more than the finer balance gains.
 constexpr int kStepBlocksPerCU = 256;
+// Small launches would otherwise give each wave a single tile, so that each
+// block's table set-up (paid once per block) weighs as much as a third of its
+// tiles' work: there every wave gets at least this many tiles, as long as
+// that still leaves four blocks per CU (else one tile per wave). On the
+// GPT-2-small list (121 k tiles) 4 or 6 take 13 % off the step, 2 and 8 a
+// little less, 16 and 32 half as much (coarser balance across the CUs).
+constexpr int kStepMinTilesPerWave = 4;
+inline unsigned step_grid(int64_t waves) {
+    const unsigned most = grid_for(waves, kStepBlocksPerCU);
+    const int64_t per_block = (int64_t)kWavesPerBlock * kStepMinTilesPerWave;
+    const int64_t thin = (waves + per_block - 1) / per_block;
+    const unsigned fill = grid_for(waves, 4);
+    const int64_t least = thin > (int64_t)fill ? thin : (int64_t)fill;
+    return (int64_t)most < least ? most : (unsigned)least;
+}
 
 // Groups of 128 and more: the whole tiles run in the table kernel, then a
 // direct-path launch covers any partial tiles. Otherwise one direct-path launch.
@@ -2143,14 +2158,14 @@ void launch_single_k1(const TensorRef& t, const StepConsts& c, hipStream_t st) {
     const int64_t tiles = (t.n + kTile - 1) / kTile, full = t.n / kTile;
     if (c.lg2_group >= 7) {
         if (full > 0)
-            hipLaunchKernelGGL((step_single_kernel<FM, FV, true, K1>), dim3(grid_for(full, kStepBlocksPerCU)),
+            hipLaunchKernelGGL((step_single_kernel<FM, FV, true, K1>), dim3(step_grid(full)),
                                dim3(kBlock), 0, st, t, c, kPhaseFull);
         if (tiles > full)
             hipLaunchKernelGGL((step_single_kernel<FM, FV, false, K1>), dim3(1), dim3(kBlock), 0, st, t, c,
                                kPhasePartial);
         return;
     }
-    hipLaunchKernelGGL((step_single_kernel<FM, FV, false, K1>), dim3(grid_for(tiles, kStepBlocksPerCU)),
+    hipLaunchKernelGGL((step_single_kernel<FM, FV, false, K1>), dim3(step_grid(tiles)),
                        dim3(kBlock), 0, st, t, c, kPhaseFull | kPhasePartial);
 }
 // Without expansion for either moment every group is stored with k = 1 after
@@ -2170,10 +2185,10 @@ void launch_multi_lg(const TensorRef* ts, const int64_t* fb, const int32_t* part
                      int64_t waves, const StepConsts& c, int phases, hipStream_t st) {
     // K1 kernels for launches without expansion (see launch_single)
     if (!c.expand_m && !c.expand_v)
-        hipLaunchKernelGGL((step_multi_kernel<FM, FV, TAB, LG, true>), dim3(grid_for(waves, kStepBlocksPerCU)),
+        hipLaunchKernelGGL((step_multi_kernel<FM, FV, TAB, LG, true>), dim3(step_grid(waves)),
                            dim3(kBlock), 0, st, ts, fb, partial, count, n_partial, c, phases);
     else
-        hipLaunchKernelGGL((step_multi_kernel<FM, FV, TAB, LG, false>), dim3(grid_for(waves, kStepBlocksPerCU)),
+        hipLaunchKernelGGL((step_multi_kernel<FM, FV, TAB, LG, false>), dim3(step_grid(waves)),
                            dim3(kBlock), 0, st, ts, fb, partial, count, n_partial, c, phases);
 }
 
